@@ -1,0 +1,408 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped rope
+term, a wrong sign or index, a transposed operand, a wrong Hadamard order or
+normalisation, a wrong slice offset, a broken merge) makes at least one fail:
+
+* library routines: scipy.linalg.hadamard, torch scaled_dot_product_attention
+  (float64, CPU), torch's float32 -> bfloat16 cast;
+* closed forms and hand-worked examples (tests/golden/worked_examples.json);
+* invariants the method states or implies (T = 1 equals MLA; a shared
+  orthogonal transform leaves scores unchanged; absorbed = un-absorbed MLA);
+* brute force with scalar Python loops on tiny inputs.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle
+from tensor_latent_decode_amd.inputs import CONFIGS, make_case
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------
+# Hadamard
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 64, 128, 512, 1024])
+def test_hadamard_matrix_is_sylvester_and_orthogonal(n):
+    h = oracle.sylvester_hadamard(n)
+    np.testing.assert_array_equal(h, scipy.linalg.hadamard(n))
+    np.testing.assert_array_equal(h @ h.T, n * np.eye(n, dtype=np.int64))
+
+
+@pytest.mark.parametrize("n", [2, 4, 16, 64, 256, 512])
+def test_fwht_equals_dense_library_product(n):
+    x = _rng(n).standard_normal((7, n))
+    dense = x @ scipy.linalg.hadamard(n).astype(np.float64) / math.sqrt(n)
+    y = oracle.fwht(x)
+    assert np.max(np.abs(y - dense)) <= 1e-12 * max(1.0, np.max(np.abs(dense)))
+
+
+def test_fwht_self_inverse_norm_preserving_and_batched():
+    x = _rng(3).standard_normal((2, 3, 512))
+    y = oracle.fwht(x)
+    np.testing.assert_allclose(oracle.fwht(y), x, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1),
+                               rtol=1e-13)
+    for i in range(2):
+        for j in range(3):
+            np.testing.assert_array_equal(y[i, j], oracle.fwht(x[i, j]))
+
+
+def test_fwht_golden():
+    for ex in json.load(open(GOLDEN))["fwht"]:
+        np.testing.assert_allclose(oracle.fwht(np.array(ex["x"], float)), ex["y"],
+                                   rtol=0, atol=1e-15)
+
+
+def test_fwht_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        oracle.fwht(np.zeros(12))
+
+
+# --------------------------------------------------------------------------
+# bf16 storage
+# --------------------------------------------------------------------------
+
+def test_bf16_round_matches_torch_cast():
+    rng = _rng(11)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32),
+        (rng.standard_normal(20000) * 1e-30).astype(np.float32),
+        (rng.standard_normal(20000) * 1e30).astype(np.float32),
+    ])
+    # exact ties: low 16 bits == 0x8000, with even and odd kept parts
+    tie_bits = (rng.integers(0, 1 << 15, 4000, dtype=np.uint32) << 16) | 0x8000
+    tie_bits = tie_bits[(tie_bits >> 23) & 0xFF != 0xFF]      # finite values only
+    x = np.concatenate([x, tie_bits.astype(np.uint32).view(np.float32),
+                        np.array([0.0, -0.0, 1.0, -1.0, 65504.0], np.float32)])
+    ours = oracle.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_bf16_bits_to_f64_matches_torch():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]          # drop inf/nan patterns
+    ours = oracle.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+# --------------------------------------------------------------------------
+# Shard attention
+# --------------------------------------------------------------------------
+
+def _sdpa(q_lat, q_rope, c_lat, k_rope, scale):
+    """Library attention: q = [q_lat || q_rope], k = [c || r], v = c."""
+    q = torch.from_numpy(np.concatenate([q_lat, q_rope], axis=1))[None, :, None, :]
+    k = torch.from_numpy(np.concatenate([c_lat, k_rope], axis=1))[None, None]
+    v = torch.from_numpy(np.ascontiguousarray(c_lat))[None, None]
+    H = q.shape[1]
+    k = k.expand(1, H, -1, -1).contiguous()
+    v = v.expand(1, H, -1, -1).contiguous()
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale)
+    return o[0, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("H,d_s,d_r,L", [(4, 32, 16, 128), (3, 8, 4, 1), (5, 16, 0, 37),
+                                         (2, 64, 64, 300)])
+def test_shard_attention_matches_library_sdpa(H, d_s, d_r, L):
+    rng = _rng(H * 1000 + L)
+    ql, qr = rng.standard_normal((H, d_s)), rng.standard_normal((H, d_r))
+    c, r = rng.standard_normal((L, d_s)), rng.standard_normal((L, d_r))
+    scale = 1.0 / math.sqrt(d_s + d_r)
+    o, _ = oracle.shard_attention(ql, qr, c, r, scale)
+    np.testing.assert_allclose(o, _sdpa(ql, qr, c, r, scale), rtol=0, atol=1e-12)
+
+
+def test_shard_attention_brute_force_loops():
+    rng = _rng(5)
+    H, d_s, d_r, L = 2, 3, 2, 5
+    ql, qr = rng.standard_normal((H, d_s)), rng.standard_normal((H, d_r))
+    c, r = rng.standard_normal((L, d_s)), rng.standard_normal((L, d_r))
+    scale = 0.37
+    o, lse = oracle.shard_attention(ql, qr, c, r, scale)
+    for h in range(H):
+        s = []
+        for j in range(L):
+            acc = math.fsum(ql[h][k] * c[j][k] for k in range(d_s))
+            acc += math.fsum(qr[h][k] * r[j][k] for k in range(d_r))
+            s.append(scale * acc)
+        z = math.fsum(math.exp(v) for v in s)
+        assert abs(lse[h] - math.log(z)) < 1e-13
+        for k in range(d_s):
+            ref = math.fsum(math.exp(s[j]) * c[j][k] for j in range(L)) / z
+            assert abs(o[h][k] - ref) < 1e-13
+
+
+def test_shard_attention_golden():
+    for ex in json.load(open(GOLDEN))["attention"]:
+        o, lse = oracle.shard_attention(np.array(ex["q_lat"]), np.array(ex["q_rope"]),
+                                        np.array(ex["c_lat"]), np.array(ex["k_rope"]),
+                                        ex["scale"])
+        np.testing.assert_allclose(o, ex["o"], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse, ex["lse"], rtol=0, atol=1e-14)
+
+
+def test_single_token_closed_form():
+    rng = _rng(6)
+    ql, qr = rng.standard_normal((4, 8)), rng.standard_normal((4, 3))
+    c, r = rng.standard_normal((1, 8)), rng.standard_normal((1, 3))
+    o, lse = oracle.shard_attention(ql, qr, c, r, 0.5)
+    np.testing.assert_allclose(o, np.repeat(c, 4, axis=0), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, 0.5 * (ql @ c[0] + qr @ r[0]), rtol=0, atol=1e-15)
+
+
+def test_zero_query_gives_mean_and_log_length():
+    rng = _rng(7)
+    L = 97
+    c, r = rng.standard_normal((L, 16)), rng.standard_normal((L, 4))
+    o, lse = oracle.shard_attention(np.zeros((3, 16)), np.zeros((3, 4)), c, r, 0.3)
+    np.testing.assert_allclose(o, np.repeat(c.mean(axis=0, keepdims=True), 3, 0),
+                               rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, np.full(3, math.log(L)), rtol=0, atol=1e-13)
+
+
+def test_empty_sequence():
+    o, lse = oracle.shard_attention(np.ones((2, 4)), np.ones((2, 2)), np.zeros((0, 4)),
+                                    np.zeros((0, 2)), 1.0)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+def test_constant_rope_key_only_shifts_lse():
+    rng = _rng(8)
+    L, H = 50, 3
+    ql, qr = rng.standard_normal((H, 8)), rng.standard_normal((H, 4))
+    c = rng.standard_normal((L, 8))
+    r_row = rng.standard_normal(4)
+    r = np.repeat(r_row[None], L, axis=0)
+    o1, lse1 = oracle.shard_attention(ql, qr, c, r, 0.4)
+    o0, lse0 = oracle.shard_attention(ql, np.zeros_like(qr), c, r, 0.4)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse1 - lse0, 0.4 * (qr @ r_row), rtol=0, atol=1e-13)
+
+
+def test_rope_term_is_not_dropped():
+    rng = _rng(9)
+    ql, qr = rng.standard_normal((2, 8)), rng.standard_normal((2, 4)) * 3
+    c, r = rng.standard_normal((20, 8)), rng.standard_normal((20, 4))
+    o1, _ = oracle.shard_attention(ql, qr, c, r, 0.5)
+    o0, _ = oracle.shard_attention(ql, np.zeros_like(qr), c, r, 0.5)
+    assert np.max(np.abs(o1 - o0)) > 1e-2
+
+
+# --------------------------------------------------------------------------
+# Split-K merge
+# --------------------------------------------------------------------------
+
+def test_merge_over_any_partition_equals_unsplit():
+    rng = _rng(10)
+    L, H = 200, 4
+    ql, qr = rng.standard_normal((H, 16)), rng.standard_normal((H, 4))
+    c, r = rng.standard_normal((L, 16)), rng.standard_normal((L, 4))
+    o_ref, lse_ref = oracle.shard_attention(ql, qr, c, r, 0.25)
+    for cuts in ([0, 200], [0, 64, 128, 200], [0, 1, 2, 3, 199, 200], [0, 0, 70, 70, 200]):
+        os_, ls_ = [], []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            o, l = oracle.shard_attention(ql, qr, c[a:b], r[a:b], 0.25)
+            os_.append(o)
+            ls_.append(l)
+        o, lse = oracle.merge_partials(os_, ls_)
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-13)
+
+
+def test_merge_all_empty():
+    o, lse = oracle.merge_partials(np.zeros((3, 2, 4)), np.full((3, 2), -np.inf))
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+# --------------------------------------------------------------------------
+# TPLA slicing and combine
+# --------------------------------------------------------------------------
+
+def test_tp1_equals_mla():
+    rng = _rng(12)
+    ql, qr = rng.standard_normal((4, 64)), rng.standard_normal((4, 16))
+    c, r = rng.standard_normal((128, 64)), rng.standard_normal((128, 16))
+    ref, _ = oracle.mla_decode(ql, qr, c, r, 0.2)
+    out = oracle.tpla_decode(ql, qr, c, r, tp=1, scale=0.2, hadamard=False)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(out, _sdpa(ql, qr, c, r, 0.2), rtol=0, atol=1e-12)
+
+
+def test_tp1_orthogonal_invariance():
+    rng = _rng(13)
+    ql, qr = rng.standard_normal((4, 64)), rng.standard_normal((4, 16))
+    c, r = rng.standard_normal((128, 64)), rng.standard_normal((128, 16))
+    ref, lse_ref = oracle.mla_decode(ql, qr, c, r, 0.2)
+    rotated = oracle.tpla_decode(ql, qr, c, r, tp=1, scale=0.2, hadamard=True)
+    back = oracle.tpla_decode(ql, qr, c, r, tp=1, scale=0.2, hadamard=True, unrotate=True)
+    np.testing.assert_allclose(back, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(rotated @ scipy.linalg.hadamard(64) / 8.0, ref, rtol=0, atol=1e-12)
+    (_, lse_rot), = oracle.tpla_shards(ql, qr, c, r, 1, 0.2, True)
+    np.testing.assert_allclose(lse_rot, lse_ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("hadamard", [False, True])
+@pytest.mark.parametrize("tp,g0", [(2, 0), (2, 1), (4, 2)])
+def test_query_on_one_shard_reduces_to_library_attention(tp, g0, hadamard):
+    """If the (rotated) latent query lives in shard g0's columns only, shard
+    g0 sees the full MLA score and its output is library attention on its
+    slice; every other shard sees only the rope score."""
+    rng = _rng(100 * tp + g0)
+    H, d_c, d_r, L = 3, 64, 8, 90
+    d_s = d_c // tp
+    q_rot = np.zeros((H, d_c))
+    q_rot[:, g0 * d_s:(g0 + 1) * d_s] = rng.standard_normal((H, d_s))
+    c_rot = rng.standard_normal((L, d_c))
+    qr, r = rng.standard_normal((H, d_r)), rng.standard_normal((L, d_r))
+    hd = scipy.linalg.hadamard(d_c).astype(float) / math.sqrt(d_c)
+    # inputs in the unrotated basis when the method rotates them itself
+    q_in, c_in = (q_rot @ hd, c_rot @ hd) if hadamard else (q_rot, c_rot)
+    scale = 0.3
+    parts = oracle.tpla_shards(q_in, qr, c_in, r, tp, scale, hadamard)
+    full = _sdpa(q_rot, qr, c_rot, r, scale)     # MLA in the rotated basis
+    for g, (o, _) in enumerate(parts):
+        sl = slice(g * d_s, (g + 1) * d_s)
+        if g == g0:
+            np.testing.assert_allclose(o, full[:, sl], rtol=0, atol=1e-11)
+        else:
+            ref = _sdpa(np.zeros((H, d_s)), qr, c_rot[:, sl], r, scale)
+            np.testing.assert_allclose(o, ref, rtol=0, atol=1e-11)
+    combined = oracle.tpla_decode(q_in, qr, c_in, r, tp, scale, hadamard)
+    np.testing.assert_allclose(combined[:, g0 * d_s:(g0 + 1) * d_s], full[:, g0 * d_s:(g0 + 1) * d_s],
+                               rtol=0, atol=1e-11)
+
+
+def test_two_shard_golden():
+    ex = json.load(open(GOLDEN))["tpla_two_shards"]
+    parts = oracle.tpla_shards(np.array(ex["q_lat"]), np.array(ex["q_rope"]),
+                               np.array(ex["c_lat"]), np.array(ex["k_rope"]),
+                               ex["tp"], ex["scale"], False)
+    np.testing.assert_allclose(parts[0][0], ex["shard0_o"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(parts[0][1], ex["shard0_lse"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(parts[1][0], ex["shard1_o"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(parts[1][1], ex["shard1_lse"], rtol=0, atol=1e-15)
+    combined = oracle.combine_shards([p[0] for p in parts])
+    assert combined.shape == (1, 4)
+    np.testing.assert_allclose(combined, ex["combined"], rtol=0, atol=1e-15)
+
+
+def test_combine_is_concatenation():
+    rng = _rng(14)
+    parts = [rng.standard_normal((2, 3, 8)) for _ in range(4)]
+    np.testing.assert_array_equal(oracle.combine_shards(parts), np.concatenate(parts, axis=-1))
+
+
+def test_absorbed_mla_equals_unabsorbed():
+    rng = _rng(15)
+    H, d_n, d_c, d_r, d_v, L = 3, 16, 32, 8, 12, 40
+    q_nope, q_rope = rng.standard_normal((H, d_n)), rng.standard_normal((H, d_r))
+    c, r = rng.standard_normal((L, d_c)), rng.standard_normal((L, d_r))
+    w_uk = rng.standard_normal((H, d_n, d_c)) / 4
+    w_uv = rng.standard_normal((H, d_v, d_c)) / 4
+    scale = 1 / math.sqrt(d_n + d_r)
+    ref = oracle.mla_decode_unabsorbed(q_nope, q_rope, c, r, w_uk, w_uv, scale)
+    q_lat = np.einsum("hn,hnc->hc", q_nope, w_uk)               # absorb W_UK into the query
+    o_lat, _ = oracle.mla_decode(q_lat, q_rope, c, r, scale)
+    out = np.einsum("hc,hvc->hv", o_lat, w_uv)                    # W_UV after attention
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Paged cache
+# --------------------------------------------------------------------------
+
+def _fill(case, dtype):
+    d_s = case.cfg.d_s
+    width = d_s + case.cfg.d_r
+    cache = np.full((case.num_blocks, case.cfg.block_size, width),
+                    0xFFFF if dtype == np.uint16 else np.nan, dtype=dtype)
+    return cache
+
+
+def test_paged_append_and_gather_roundtrip_and_permutation_invariance():
+    case = make_case(CONFIGS["tiny_fp32"], block_size=16, batch=3, ctx=(20, 70), seed=21)
+    d_s = case.cfg.d_s
+    for g in range(case.cfg.tp):
+        lat = case.hist_latent[:, g * d_s:(g + 1) * d_s]
+        cache = _fill(case, np.float32)
+        oracle.paged_append(cache, case.block_table, 16, case.hist_seq, case.hist_pos,
+                            lat, case.hist_rope)
+        # a different physical placement of the same logical rows
+        perm = np.random.default_rng(3).permutation(case.num_blocks - 1)
+        bt2 = np.where(case.block_table == case.num_blocks - 1, case.num_blocks - 1,
+                       perm[np.minimum(case.block_table, case.num_blocks - 2)])
+        cache2 = _fill(case, np.float32)
+        oracle.paged_append(cache2, bt2, 16, case.hist_seq, case.hist_pos, lat, case.hist_rope)
+        off = 0
+        for b in range(case.cfg.batch):
+            n = int(case.seq_lens[b]) - 1
+            rows = oracle.gather_sequence(cache, case.block_table, b, n, 16)
+            rows2 = oracle.gather_sequence(cache2, bt2, b, n, 16)
+            np.testing.assert_array_equal(rows[:, :d_s], lat[off:off + n])
+            np.testing.assert_array_equal(rows[:, d_s:], case.hist_rope[off:off + n])
+            np.testing.assert_array_equal(rows, rows2)
+            off += n
+        # unused slots were never written
+        used = set()
+        for b in range(case.cfg.batch):
+            for j in range(int(case.seq_lens[b]) - 1):
+                used.add(oracle.page_slot(case.block_table, b, j, 16))
+        flat = cache.reshape(-1, cache.shape[-1])
+        unused = [s for s in range(flat.shape[0]) if s not in used]
+        assert np.all(np.isnan(flat[unused]))
+
+
+def test_paged_append_bf16_bits_and_fp32_source_rounding():
+    case = make_case(CONFIGS["dsv3_4k"], ctx=100, seed=22, heads=4)
+    cache = np.full((case.num_blocks, 64, 320), 0xFFFF, np.uint16)
+    lat = case.hist_latent[:, :256]
+    oracle.paged_append(cache, case.block_table, 64, case.hist_seq, case.hist_pos,
+                        lat, case.hist_rope)
+    rows = cache.reshape(-1, 320)[[oracle.page_slot(case.block_table, 0, j, 64)
+                                   for j in range(99)]]
+    np.testing.assert_array_equal(rows[:, :256], lat)
+    src = np.random.default_rng(1).standard_normal((1, 256)).astype(np.float32)
+    oracle.paged_append(cache, case.block_table, 64, np.array([0]), np.array([99]),
+                        src, np.zeros((1, 64), np.float32))
+    got = cache.reshape(-1, 320)[oracle.page_slot(case.block_table, 0, 99, 64), :256]
+    ref = torch.from_numpy(src[0]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_paged_decode_matches_logical_decode():
+    case = make_case(CONFIGS["tiny_fp32"], batch=2, ctx=(60, 130), seed=23, block_size=16)
+    cfg = case.cfg
+    d_s = cfg.d_s
+    for g in range(cfg.tp):
+        cache = _fill(case, np.float32)
+        oracle.paged_append(cache, case.block_table, 16, case.hist_seq, case.hist_pos,
+                            case.hist_latent[:, g * d_s:(g + 1) * d_s], case.hist_rope)
+        lens = case.seq_lens - 1
+        ql = case.q_latent[..., g * d_s:(g + 1) * d_s]
+        o, lse = oracle.tpla_decode_paged(ql, case.q_rope, cache, case.block_table, lens,
+                                          16, d_s, cfg.scale)
+        off = 0
+        for b in range(cfg.batch):
+            n = int(lens[b])
+            ref_o, ref_l = oracle.shard_attention(
+                ql[b], case.q_rope[b], case.hist_latent[off:off + n, g * d_s:(g + 1) * d_s],
+                case.hist_rope[off:off + n], cfg.scale)
+            np.testing.assert_array_equal(o[b], ref_o)
+            np.testing.assert_array_equal(lse[b], ref_l)
+            off += n
