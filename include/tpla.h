@@ -1,0 +1,225 @@
+/*
+ * tpla.h - C ABI of libtpla.so: TPLA decode attention on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method (arXiv 2508.15881, "TPLA: Tensor Parallel Latent Attention for
+ * Efficient Disaggregated Prefill & Decode Inference"; English abstract on
+ * the chatpaper.ai / fugumt.com / searcharxiv.org pages, revised abstract on
+ * the paperbot-e5f.pages.dev page, and the blogs.edgentiq.com article):
+ * MLA caches one low-rank latent vector cKV per token.  TPLA splits that
+ * latent, and every head's input dimension (the absorbed query), across
+ * tensor-parallel devices.  Each device attends over the whole sequence with
+ * all heads, using only its latent slice, and the devices sum their results
+ * with an all-reduce.  An orthogonal transform (Hadamard) applied to query
+ * and latent before the split reduces the error between shards.  Decode is
+ * memory bound, so the latent cache each device streams is the cost.
+ *
+ * One call of tpla_decode_shard is one device's share of one decode step:
+ * every head, every sequence, one latent slice.
+ *
+ * Conventions for every entry point:
+ *  - The caller owns all memory.  Pointers marked "device" point to GPU
+ *    memory of the current HIP device.  The library allocates nothing; the
+ *    decode call takes a caller-provided workspace (size query below).
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *    Every call only enqueues work on it and returns; none synchronises.
+ *  - Sizes and strides are counted in elements, not bytes.
+ *  - Host-visible arguments are checked before anything is enqueued; a
+ *    failed check returns a non-zero status, enqueues nothing, and leaves
+ *    a message for tpla_last_error().  A HIP launch error returns
+ *    TPLA_ERR_HIP.  Device-resident data (block ids, positions, lengths)
+ *    are not read by the host; kernels skip rows whose position or block id
+ *    is out of range, so bad device data gives unspecified results but no
+ *    access outside the buffers described here.
+ *  - bf16 means IEEE binary32 truncated to its top 16 bits (uint16 storage);
+ *    every float32 -> bf16 conversion rounds to nearest, ties to even.
+ *  - No function throws; all are thread-safe (the error text is per thread).
+ */
+#ifndef TPLA_H_
+#define TPLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tpla_status {
+  TPLA_OK = 0,
+  TPLA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  TPLA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent          */
+  TPLA_ERR_ALIGN = 3,       /* pointer/stride alignment the kernel needs       */
+  TPLA_ERR_DTYPE = 4,       /* unsupported element type or combination         */
+  TPLA_ERR_UNSUPPORTED = 5, /* valid request this build has no kernel for      */
+  TPLA_ERR_WORKSPACE = 6,   /* workspace missing or too small                  */
+  TPLA_ERR_HIP = 7          /* the HIP runtime reported an error               */
+} tpla_status;
+
+typedef enum tpla_dtype {
+  TPLA_FP32 = 0,
+  TPLA_BF16 = 1
+} tpla_dtype;
+
+/*
+ * tpla_hadamard_latent: y[r, :] = x[r, :] . H_n / sqrt(n) for r < rows.
+ *
+ * The orthogonal transform TPLA applies to the absorbed query and to the
+ * latent before slicing them across devices (abstract: Hadamard before TP
+ * slicing; edgentiq blog, section "How TPLA Works: Smart Slicing and
+ * Reparameterization").  H_n is Sylvester's Hadamard matrix in natural
+ * order (H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]]), so the map is
+ * orthonormal, symmetric and its own inverse: calling it on the combined
+ * output rotates that back.
+ *
+ *  x, y        device, rows x n elements, row r at x + r*x_row_stride.
+ *              x == y (same rows, same strides) is allowed; other overlaps
+ *              are not.
+ *  x_dtype,
+ *  y_dtype     TPLA_FP32 or TPLA_BF16, any combination.  Arithmetic is
+ *              float32; the result is rounded once to y_dtype.
+ *  n           power of two, 1 <= n <= 4096.
+ *  strides     >= n.
+ * Errors: TPLA_ERR_NULL (x or y NULL with rows > 0), TPLA_ERR_SHAPE (n not
+ * a power of two or > 4096, rows < 0, stride < n), TPLA_ERR_DTYPE.
+ * rows == 0 is a no-op.
+ */
+tpla_status tpla_hadamard_latent(const void* x, tpla_dtype x_dtype, int64_t x_row_stride,
+                                 void* y, tpla_dtype y_dtype, int64_t y_row_stride,
+                                 int64_t rows, int32_t n, void* stream);
+
+/*
+ * tpla_append_kv: write new rows into one shard's paged latent cache.
+ *
+ * MLA caches only the latent cKV (plus the shared rope key); under TPLA a
+ * device caches only its latent slice (abstract; paperbot revised abstract).
+ * For each row t < n_rows, with b = row_seq[t] and p = row_pos[t]:
+ *     slot = block_table[b*max_blocks_per_seq + p/block_size]*block_size
+ *            + p % block_size
+ *     cache[slot, 0:d_s]       = latent[t*latent_row_stride + 0 .. d_s)
+ *     cache[slot, d_s:d_s+d_r] = rope  [t*rope_row_stride   + 0 .. d_r)
+ * The caller passes `latent` already offset to its shard's columns
+ * (g*d_s for shard g of a row of width d_c).
+ *
+ *  cache        device, [num_blocks, block_size, d_s + d_r], cache_dtype.
+ *  block_table  device int32 [batch, max_blocks_per_seq].
+ *  row_seq,
+ *  row_pos      device int32 [n_rows].
+ *  latent,rope  device, src_dtype.  rope may be NULL only if d_r == 0.
+ *  Conversion: same type -> bit copy; float32 -> bf16 rounds to nearest
+ *  even; bf16 -> float32 is exact.
+ *  Rows with b outside [0, batch), p outside [0, max_blocks_per_seq *
+ *  block_size) or a block id outside [0, num_blocks) are skipped.  Two rows
+ *  that map to the same slot race.
+ * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE (non-positive sizes, n_rows < 0,
+ * strides shorter than a row), TPLA_ERR_DTYPE.  n_rows == 0 is a no-op.
+ */
+tpla_status tpla_append_kv(void* cache, tpla_dtype cache_dtype, int32_t num_blocks,
+                           int32_t block_size, int32_t d_s, int32_t d_r,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           int32_t batch, const int32_t* row_seq, const int32_t* row_pos,
+                           int32_t n_rows, const void* latent, int64_t latent_row_stride,
+                           const void* rope, int64_t rope_row_stride, tpla_dtype src_dtype,
+                           void* stream);
+
+/*
+ * Arguments of one shard's decode step (see tpla_decode_shard).
+ */
+typedef struct tpla_decode_args {
+  int32_t batch;               /* sequences                                     */
+  int32_t heads;               /* query heads; all of them run on every shard   */
+  int32_t d_s;                 /* latent slice width of this shard (d_c / tp)   */
+  int32_t d_r;                 /* rope width (0 allowed)                        */
+  int32_t block_size;          /* cache rows per physical block                 */
+  int32_t num_blocks;          /* physical blocks in `cache`                    */
+  int32_t max_blocks_per_seq;  /* columns of `block_table`                      */
+  int32_t max_seq_len;         /* host-side bound: seq_lens[b] <= max_seq_len   */
+  tpla_dtype dtype;            /* element type of q_latent, q_rope and cache    */
+  float scale;                 /* softmax scale applied to the whole score      */
+  const void* q_latent;        /* device, absorbed query slice; element (b,h,k) */
+  int64_t q_latent_stride_b;   /*   at q_latent + b*stride_b + h*stride_h + k   */
+  int64_t q_latent_stride_h;
+  const void* q_rope;          /* device, rope query, (b,h,k) as above          */
+  int64_t q_rope_stride_b;
+  int64_t q_rope_stride_h;
+  const void* cache;           /* device, [num_blocks, block_size, d_s + d_r]   */
+  const int32_t* block_table;  /* device int32 [batch, max_blocks_per_seq]      */
+  const int32_t* seq_lens;     /* device int32 [batch], tokens to attend over   */
+  void* out;                   /* device, (b,h,k) at out + b*sb + h*sh + k      */
+  tpla_dtype out_dtype;
+  int64_t out_stride_b;
+  int64_t out_stride_h;
+  float* lse;                  /* device float32 [batch, heads] or NULL         */
+  int32_t num_splits;          /* token splits per sequence; 0 = automatic      */
+} tpla_decode_args;
+
+/*
+ * tpla_decode_workspace_size: bytes of device workspace tpla_decode_shard
+ * needs for `args` (same args => same size, on the same device).
+ * Errors: as tpla_decode_shard's argument checks; TPLA_ERR_HIP if the device
+ * cannot be queried.
+ */
+tpla_status tpla_decode_workspace_size(const tpla_decode_args* args, size_t* bytes);
+
+/*
+ * tpla_decode_shard: one device's share of a TPLA decode step.
+ *
+ * Per-shard attention with the shard's own softmax (abstract: attention is
+ * performed independently per shard; edgentiq blog, "How TPLA Works": the
+ * global score is approximated from local computations).  For every
+ * sequence b < batch and head h < heads, with L = seq_lens[b] and the
+ * cache row of logical token j read through the block table,
+ *     s_j  = scale * ( q_latent[b,h,:] . row_j[0:d_s]
+ *                    + q_rope[b,h,:]   . row_j[d_s:d_s+d_r] )
+ *     out[b,h,:] = sum_j softmax(s)_j * row_j[0:d_s]
+ *     lse[b,h]   = log sum_j exp(s_j)
+ * The rope part is whole on every shard; only the latent is sliced.
+ * L == 0 gives out = 0 and lse = -inf.  Tokens j >= L are never read.
+ *
+ * The work is split over tokens; each split keeps a running max and sum
+ * (online softmax) and the splits are merged by log-sum-exp before `out` is
+ * written.
+ *
+ * Requirements: dtype BF16 with heads % 32 == 0, d_s % 32 == 0, d_r % 16 == 0,
+ * 16-byte aligned q/cache pointers and strides that are multiples of 8 use
+ * the bf16 matrix-core kernel; every other shape (and FP32) runs a plain
+ * float32 kernel.  d_s + d_r <= 1024.  out_dtype FP32 or BF16.
+ * workspace: device, at least tpla_decode_workspace_size() bytes, 256-byte
+ * aligned; its contents on entry do not matter.
+ * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE, TPLA_ERR_DTYPE, TPLA_ERR_WORKSPACE,
+ * TPLA_ERR_HIP.
+ */
+tpla_status tpla_decode_shard(const tpla_decode_args* args, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * tpla_combine_shards: the all-reduce of the shard outputs, on one device.
+ *
+ * Shards hold disjoint latent columns, so the sum of the zero-padded shard
+ * outputs is their placement side by side (abstract: results are combined
+ * with an all-reduce):
+ *     out[b, h, g*d_s + k] = (accumulate ? out[b, h, g*d_s + k] : 0)
+ *                            + partials[g][(b*heads + h)*d_s + k]
+ * partials: HOST array of tp device pointers, each [batch, heads, d_s]
+ * contiguous, part_dtype.  out: device [batch, heads, tp*d_s] contiguous.
+ * With accumulate == 0 the values are copied (bit exact for equal types,
+ * nearest-even for float32 -> bf16).
+ * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE (tp outside [1, 16], sizes < 1),
+ * TPLA_ERR_DTYPE.
+ */
+tpla_status tpla_combine_shards(const void* const* partials, tpla_dtype part_dtype, int32_t tp,
+                                int32_t batch, int32_t heads, int32_t d_s, void* out,
+                                tpla_dtype out_dtype, int32_t accumulate, void* stream);
+
+/* Static text for a status code. */
+const char* tpla_status_string(tpla_status status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* tpla_last_error(void);
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t tpla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPLA_H_ */

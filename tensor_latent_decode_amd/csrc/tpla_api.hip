@@ -1,0 +1,304 @@
+// Host side of the libtpla C ABI: argument checks, split planning and
+// kernel dispatch.  Nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "tpla.h"
+#include "tpla_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tpla_status fail(tpla_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+tpla_status ok() {
+  g_err[0] = '\0';
+  return TPLA_OK;
+}
+
+tpla_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TPLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_dtype(tpla_dtype d) { return d == TPLA_FP32 || d == TPLA_BF16; }
+bool is_pow2(int64_t n) { return n > 0 && (n & (n - 1)) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute units of the current device, cached per device id.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+tpla_status device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *cus = cached;
+      return TPLA_OK;
+    }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_status(e, "hipDeviceGetAttribute");
+  if (n <= 0) n = 1;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  *cus = n;
+  return TPLA_OK;
+}
+
+constexpr int64_t kMaxGenericSmem = 65536;
+
+int64_t generic_smem(int d_s, int d_r) {
+  return static_cast<int64_t>(sizeof(float)) * (16LL * (d_s + d_r) + 8LL * (d_s + d_r) + 8LL * d_s + 8 * 16 + 8 * 3);
+}
+
+bool use_mfma(const tpla_decode_args* a) {
+  if (a->dtype != TPLA_BF16) return false;
+  if (!tpla::decode_mfma_supported(a->heads, a->d_s, a->d_r)) return false;
+  if (!aligned16(a->q_latent) || !aligned16(a->cache)) return false;
+  if ((a->q_latent_stride_b | a->q_latent_stride_h) % 8 != 0) return false;
+  if (a->d_r > 0) {
+    if (!aligned16(a->q_rope)) return false;
+    if ((a->q_rope_stride_b | a->q_rope_stride_h) % 8 != 0) return false;
+  }
+  return true;
+}
+
+tpla_status check_decode(const tpla_decode_args* a) {
+  if (a == nullptr) return fail(TPLA_ERR_NULL, "args is NULL");
+  if (a->batch < 1 || a->heads < 1 || a->d_s < 1 || a->d_r < 0)
+    return fail(TPLA_ERR_SHAPE, "batch, heads, d_s must be >= 1 and d_r >= 0");
+  if (a->block_size < 1 || a->num_blocks < 1 || a->max_blocks_per_seq < 1)
+    return fail(TPLA_ERR_SHAPE, "block_size, num_blocks, max_blocks_per_seq must be >= 1");
+  if (a->max_seq_len < 0 ||
+      static_cast<int64_t>(a->max_seq_len) >
+          static_cast<int64_t>(a->max_blocks_per_seq) * a->block_size)
+    return fail(TPLA_ERR_SHAPE, "max_seq_len must be in [0, max_blocks_per_seq*block_size]");
+  if (!valid_dtype(a->dtype) || !valid_dtype(a->out_dtype))
+    return fail(TPLA_ERR_DTYPE, "dtype/out_dtype must be TPLA_FP32 or TPLA_BF16");
+  if (!(a->scale == a->scale) || std::isinf(a->scale))
+    return fail(TPLA_ERR_SHAPE, "scale must be finite");
+  if (a->q_latent == nullptr || a->cache == nullptr || a->block_table == nullptr ||
+      a->seq_lens == nullptr || a->out == nullptr)
+    return fail(TPLA_ERR_NULL, "q_latent, cache, block_table, seq_lens and out are required");
+  if (a->d_r > 0 && a->q_rope == nullptr) return fail(TPLA_ERR_NULL, "q_rope is NULL with d_r > 0");
+  if (a->num_splits < 0) return fail(TPLA_ERR_SHAPE, "num_splits must be >= 0");
+  if (a->q_latent_stride_h < a->d_s || a->q_latent_stride_b < 0 || a->q_rope_stride_b < 0 ||
+      (a->d_r > 0 && a->q_rope_stride_h < a->d_r) ||
+      a->out_stride_h < a->d_s || a->out_stride_b < 0)
+    return fail(TPLA_ERR_SHAPE, "query/output head strides must cover a row");
+  if (!use_mfma(a) && generic_smem(a->d_s, a->d_r) > kMaxGenericSmem)
+    return fail(TPLA_ERR_UNSUPPORTED,
+                "d_s=%d d_r=%d has no bf16 matrix-core kernel and exceeds the float32 "
+                "kernel's LDS limit",
+                a->d_s, a->d_r);
+  return TPLA_OK;
+}
+
+struct Plan {
+  int splits;
+  int chunk;
+  size_t ws_o_bytes;
+  size_t ws_bytes;
+};
+
+tpla_status plan_decode(const tpla_decode_args* a, Plan* pl) {
+  const int maxlen = a->max_seq_len;
+  int want = a->num_splits;
+  if (want == 0) {
+    int cus = 0;
+    const tpla_status st = device_cus(&cus);
+    if (st != TPLA_OK) return st;
+    int64_t groups = a->batch;
+    int per_cu = 2;
+    if (use_mfma(a)) {
+      groups *= a->heads / (32 * (a->heads % 128 == 0 ? 4 : (a->heads % 64 == 0 ? 2 : 1)));
+      per_cu = tpla::decode_mfma_groups_per_cu(a->heads, a->d_s, a->d_r);
+    } else {
+      groups *= (a->heads + 7) / 8;
+    }
+    const int64_t target = static_cast<int64_t>(cus) * per_cu;
+    want = static_cast<int>(std::max<int64_t>(1, (target + groups - 1) / groups));
+  }
+  const int max_tiles = std::max(1, (maxlen + 63) / 64);
+  want = std::min(want, max_tiles);
+  const int tiles_per = (max_tiles + want - 1) / want;
+  pl->chunk = tiles_per * 64;
+  pl->splits = std::max(1, (maxlen + pl->chunk - 1) / pl->chunk);
+  const size_t rows = static_cast<size_t>(pl->splits) * a->batch * a->heads;
+  pl->ws_o_bytes = (rows * a->d_s * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  pl->ws_bytes = pl->ws_o_bytes + ((rows * sizeof(float) + 255) & ~static_cast<size_t>(255));
+  return TPLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tpla_status_string(tpla_status s) {
+  switch (s) {
+    case TPLA_OK: return "ok";
+    case TPLA_ERR_NULL: return "null pointer";
+    case TPLA_ERR_SHAPE: return "bad shape or size";
+    case TPLA_ERR_ALIGN: return "bad alignment";
+    case TPLA_ERR_DTYPE: return "unsupported dtype";
+    case TPLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TPLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case TPLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* tpla_last_error(void) { return g_err; }
+
+int32_t tpla_version(void) { return 100; }
+
+tpla_status tpla_hadamard_latent(const void* x, tpla_dtype x_dtype, int64_t x_row_stride, void* y,
+                                 tpla_dtype y_dtype, int64_t y_row_stride, int64_t rows, int32_t n,
+                                 void* stream) {
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype))
+    return fail(TPLA_ERR_DTYPE, "x_dtype/y_dtype must be TPLA_FP32 or TPLA_BF16");
+  if (!is_pow2(n) || n > 4096) return fail(TPLA_ERR_SHAPE, "n=%d must be a power of two <= 4096", n);
+  if (rows < 0) return fail(TPLA_ERR_SHAPE, "rows must be >= 0");
+  if (x_row_stride < n || y_row_stride < n)
+    return fail(TPLA_ERR_SHAPE, "row strides must be >= n");
+  if (rows == 0) return ok();
+  if (x == nullptr || y == nullptr) return fail(TPLA_ERR_NULL, "x and y are required");
+  return hip_status(tpla::launch_hadamard(x, x_dtype == TPLA_BF16, x_row_stride, y,
+                                          y_dtype == TPLA_BF16, y_row_stride, rows, n,
+                                          static_cast<hipStream_t>(stream)),
+                    "hadamard launch");
+}
+
+tpla_status tpla_append_kv(void* cache, tpla_dtype cache_dtype, int32_t num_blocks,
+                           int32_t block_size, int32_t d_s, int32_t d_r,
+                           const int32_t* block_table, int32_t max_blocks_per_seq, int32_t batch,
+                           const int32_t* row_seq, const int32_t* row_pos, int32_t n_rows,
+                           const void* latent, int64_t latent_row_stride, const void* rope,
+                           int64_t rope_row_stride, tpla_dtype src_dtype, void* stream) {
+  if (!valid_dtype(cache_dtype) || !valid_dtype(src_dtype))
+    return fail(TPLA_ERR_DTYPE, "cache_dtype/src_dtype must be TPLA_FP32 or TPLA_BF16");
+  if (num_blocks < 1 || block_size < 1 || d_s < 1 || d_r < 0 || max_blocks_per_seq < 1 ||
+      batch < 1 || n_rows < 0)
+    return fail(TPLA_ERR_SHAPE, "non-positive size");
+  if (latent_row_stride < d_s || (d_r > 0 && rope_row_stride < d_r))
+    return fail(TPLA_ERR_SHAPE, "source row strides must cover a row");
+  if (n_rows == 0) return ok();
+  if (cache == nullptr || block_table == nullptr || row_seq == nullptr || row_pos == nullptr ||
+      latent == nullptr || (d_r > 0 && rope == nullptr))
+    return fail(TPLA_ERR_NULL, "cache, block_table, row_seq, row_pos, latent (and rope) are required");
+  return hip_status(
+      tpla::launch_append(cache, cache_dtype == TPLA_BF16, num_blocks, block_size, d_s, d_r,
+                          block_table, max_blocks_per_seq, batch, row_seq, row_pos, n_rows, latent,
+                          latent_row_stride, rope, rope_row_stride, src_dtype == TPLA_BF16,
+                          static_cast<hipStream_t>(stream)),
+      "append launch");
+}
+
+tpla_status tpla_decode_workspace_size(const tpla_decode_args* args, size_t* bytes) {
+  if (bytes == nullptr) return fail(TPLA_ERR_NULL, "bytes is NULL");
+  tpla_status st = check_decode(args);
+  if (st != TPLA_OK) return st;
+  Plan pl;
+  st = plan_decode(args, &pl);
+  if (st != TPLA_OK) return st;
+  *bytes = pl.ws_bytes;
+  return ok();
+}
+
+tpla_status tpla_decode_shard(const tpla_decode_args* a, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  tpla_status st = check_decode(a);
+  if (st != TPLA_OK) return st;
+  Plan pl;
+  st = plan_decode(a, &pl);
+  if (st != TPLA_OK) return st;
+  if (workspace == nullptr || workspace_bytes < pl.ws_bytes)
+    return fail(TPLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", pl.ws_bytes,
+                workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(TPLA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  tpla::DecodeParams p{};
+  p.batch = a->batch;
+  p.heads = a->heads;
+  p.d_s = a->d_s;
+  p.d_r = a->d_r;
+  p.block_size = a->block_size;
+  p.num_blocks = a->num_blocks;
+  p.max_blocks = a->max_blocks_per_seq;
+  p.max_seq_len = a->max_seq_len;
+  p.num_splits = pl.splits;
+  p.chunk = pl.chunk;
+  p.scale_log2 = a->scale * 1.4426950408889634f;
+  p.q_latent = a->q_latent;
+  p.qls_b = a->q_latent_stride_b;
+  p.qls_h = a->q_latent_stride_h;
+  p.q_rope = a->q_rope;
+  p.qrs_b = a->q_rope_stride_b;
+  p.qrs_h = a->q_rope_stride_h;
+  p.cache = a->cache;
+  p.block_table = a->block_table;
+  p.seq_lens = a->seq_lens;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_o_bytes);
+
+  hipError_t e;
+  if (use_mfma(a)) {
+    e = tpla::launch_decode_mfma(p, s);
+  } else {
+    e = tpla::launch_decode_generic(p, a->dtype == TPLA_BF16, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "decode launch");
+
+  tpla::MergeParams m{};
+  m.splits = pl.splits;
+  m.batch = a->batch;
+  m.heads = a->heads;
+  m.d_s = a->d_s;
+  m.ws_o = p.ws_o;
+  m.ws_lse = p.ws_lse;
+  m.out = a->out;
+  m.out_bf16 = a->out_dtype == TPLA_BF16;
+  m.out_sb = a->out_stride_b;
+  m.out_sh = a->out_stride_h;
+  m.lse = a->lse;
+  return hip_status(tpla::launch_merge(m, s), "merge launch");
+}
+
+tpla_status tpla_combine_shards(const void* const* partials, tpla_dtype part_dtype, int32_t tp,
+                                int32_t batch, int32_t heads, int32_t d_s, void* out,
+                                tpla_dtype out_dtype, int32_t accumulate, void* stream) {
+  if (!valid_dtype(part_dtype) || !valid_dtype(out_dtype))
+    return fail(TPLA_ERR_DTYPE, "part_dtype/out_dtype must be TPLA_FP32 or TPLA_BF16");
+  if (tp < 1 || tp > tpla::kMaxTp) return fail(TPLA_ERR_SHAPE, "tp=%d must be in [1, 16]", tp);
+  if (batch < 1 || heads < 1 || d_s < 1) return fail(TPLA_ERR_SHAPE, "non-positive size");
+  if (partials == nullptr || out == nullptr) return fail(TPLA_ERR_NULL, "partials and out are required");
+  tpla::PartPtrs pp{};
+  for (int g = 0; g < tp; ++g) {
+    if (partials[g] == nullptr) return fail(TPLA_ERR_NULL, "partials[%d] is NULL", g);
+    pp.p[g] = partials[g];
+  }
+  return hip_status(tpla::launch_combine(pp, part_dtype == TPLA_BF16, tp, batch, heads, d_s, out,
+                                         out_dtype == TPLA_BF16, accumulate != 0,
+                                         static_cast<hipStream_t>(stream)),
+                    "combine launch");
+}
+
+}  // extern "C"

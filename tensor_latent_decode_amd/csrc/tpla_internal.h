@@ -1,0 +1,90 @@
+// Internal declarations shared by the libtpla translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tpla.h"
+
+namespace tpla {
+
+// ---------------------------------------------------------------------------
+// bf16 <-> float32 on the device.  bf16 values travel as uint16_t bit
+// patterns; conversions to bf16 round to nearest, ties to even.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u) {
+    return static_cast<uint16_t>((u >> 16) | 0x0040u);  // quiet NaN, sign kept
+  }
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static void store(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// ---------------------------------------------------------------------------
+// Decode kernel parameters (device pointers and sizes after validation).
+// ---------------------------------------------------------------------------
+struct DecodeParams {
+  int batch, heads, d_s, d_r;
+  int block_size, num_blocks, max_blocks;
+  int max_seq_len;
+  int num_splits, chunk;        // tokens per split, multiple of 64
+  float scale_log2;             // scale * log2(e)
+  const void* q_latent;
+  int64_t qls_b, qls_h;
+  const void* q_rope;
+  int64_t qrs_b, qrs_h;
+  const void* cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* ws_o;                  // [splits, batch, heads, d_s]
+  float* ws_lse;                // [splits, batch, heads]
+};
+
+struct MergeParams {
+  int splits, batch, heads, d_s;
+  const float* ws_o;
+  const float* ws_lse;
+  void* out;
+  int out_bf16;
+  int64_t out_sb, out_sh;
+  float* lse;
+};
+
+constexpr int kMaxTp = 16;
+struct PartPtrs {
+  const void* p[kMaxTp];
+};
+
+// Launchers (return the launch status; they do not synchronise).
+hipError_t launch_hadamard(const void* x, int x_bf16, int64_t xs, void* y, int y_bf16, int64_t ys,
+                           int64_t rows, int n, hipStream_t s);
+hipError_t launch_append(void* cache, int cache_bf16, int num_blocks, int block_size, int d_s,
+                         int d_r, const int32_t* bt, int max_blocks, int batch,
+                         const int32_t* row_seq, const int32_t* row_pos, int n_rows,
+                         const void* latent, int64_t ls, const void* rope, int64_t rs,
+                         int src_bf16, hipStream_t s);
+// Returns hipErrorNotSupported when no matrix-core instantiation fits.
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s);
+bool decode_mfma_supported(int heads, int d_s, int d_r);
+int decode_mfma_groups_per_cu(int heads, int d_s, int d_r);
+hipError_t launch_decode_generic(const DecodeParams& p, int is_bf16, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+hipError_t launch_combine(const PartPtrs& parts, int part_bf16, int tp, int batch, int heads,
+                          int d_s, void* out, int out_bf16, int accumulate, hipStream_t s);
+
+}  // namespace tpla

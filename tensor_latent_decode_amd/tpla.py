@@ -1,0 +1,287 @@
+"""Python binding of libtpla.so (ctypes).
+
+Argument marshalling only: every computation runs in the library's HIP
+kernels.  torch supplies device memory (tensors) and the current stream.
+Functions raise TplaError on a non-zero status.  If the library has not been
+built the first call raises RuntimeError; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtpla.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tpla.h")
+
+FP32, BF16 = 0, 1
+STATUS = {0: "TPLA_OK", 1: "TPLA_ERR_NULL", 2: "TPLA_ERR_SHAPE", 3: "TPLA_ERR_ALIGN",
+          4: "TPLA_ERR_DTYPE", 5: "TPLA_ERR_UNSUPPORTED", 6: "TPLA_ERR_WORKSPACE",
+          7: "TPLA_ERR_HIP"}
+
+
+class TplaError(RuntimeError):
+    def __init__(self, func: str, status: int, message: str):
+        self.status = status
+        super().__init__(f"{func}: {STATUS.get(status, status)}: {message}")
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of tpla_decode_args (include/tpla.h)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("d_s", ctypes.c_int32),
+        ("d_r", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32), ("dtype", ctypes.c_int), ("scale", ctypes.c_float),
+        ("q_latent", ctypes.c_void_p), ("q_latent_stride_b", ctypes.c_int64),
+        ("q_latent_stride_h", ctypes.c_int64),
+        ("q_rope", ctypes.c_void_p), ("q_rope_stride_b", ctypes.c_int64),
+        ("q_rope_stride_h", ctypes.c_int64),
+        ("cache", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int),
+        ("out_stride_b", ctypes.c_int64), ("out_stride_h", ctypes.c_int64),
+        ("lse", ctypes.c_void_p), ("num_splits", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtpla.so once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m tensor_latent_decode_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    dt = ctypes.c_int
+    L.tpla_hadamard_latent.argtypes = [vp, dt, i64, vp, dt, i64, i64, i32, vp]
+    L.tpla_append_kv.argtypes = [vp, dt, i32, i32, i32, i32, vp, i32, i32, vp, vp, i32, vp, i64,
+                                 vp, i64, dt, vp]
+    L.tpla_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(sz)]
+    L.tpla_decode_shard.argtypes = [ctypes.POINTER(DecodeArgs), vp, sz, vp]
+    L.tpla_combine_shards.argtypes = [ctypes.POINTER(vp), dt, i32, i32, i32, i32, vp, dt, i32, vp]
+    for f in ("tpla_hadamard_latent", "tpla_append_kv", "tpla_decode_workspace_size",
+              "tpla_decode_shard", "tpla_combine_shards"):
+        getattr(L, f).restype = ctypes.c_int
+    L.tpla_status_string.argtypes = [ctypes.c_int]
+    L.tpla_status_string.restype = ctypes.c_char_p
+    L.tpla_last_error.argtypes = []
+    L.tpla_last_error.restype = ctypes.c_char_p
+    L.tpla_version.argtypes = []
+    L.tpla_version.restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+def header_functions() -> List[str]:
+    """Names of the functions include/tpla.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tpla_[a-z_0-9]+)\s*\(", text)))
+
+
+def _check(name: str, status: int) -> None:
+    if status != 0:
+        raise TplaError(name, status, lib().tpla_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FP32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _dt_of(dtype: torch.dtype) -> int:
+    return _dt(torch.empty(0, dtype=dtype))
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _gpu(*ts: Optional[torch.Tensor]) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def _rows(x: torch.Tensor):
+    """(rows, n, row_stride) of a tensor whose leading dims collapse to one."""
+    if x.dim() < 1 or x.stride(-1) != 1:
+        raise ValueError("last dimension must be contiguous")
+    n = x.shape[-1]
+    if x.dim() == 1:
+        return 1, n, n
+    try:
+        flat = x.view(-1, n)
+    except RuntimeError as e:
+        raise ValueError("rows must be addressable with a single row stride") from e
+    return flat.shape[0], n, (flat.stride(0) if flat.shape[0] > 1 else n)
+
+
+def hadamard_latent(x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """out[..., :] = x[..., :] @ H_n / sqrt(n) over the last dimension."""
+    _gpu(x, out)
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    rows, n, xs = _rows(x)
+    _, _, ys = _rows(out)
+    _check("tpla_hadamard_latent",
+           lib().tpla_hadamard_latent(x.data_ptr(), _dt(x), xs, out.data_ptr(), _dt(out), ys,
+                                      rows, n, _stream(x)))
+    return out
+
+
+def append_kv(cache: torch.Tensor, block_table: torch.Tensor, row_seq: torch.Tensor,
+              row_pos: torch.Tensor, latent: torch.Tensor, rope: Optional[torch.Tensor],
+              batch: Optional[int] = None) -> None:
+    """Write rows [latent_t || rope_t] into the paged cache [blocks, bs, d_s + d_r]."""
+    _gpu(cache, block_table, row_seq, row_pos, latent, rope)
+    if rope is not None and rope.shape[-1] == 0:
+        rope = None
+    num_blocks, bs, width = cache.shape
+    d_s = latent.shape[-1]
+    d_r = 0 if rope is None else rope.shape[-1]
+    if width != d_s + d_r or not cache.is_contiguous():
+        raise ValueError("cache must be contiguous [num_blocks, block_size, d_s + d_r]")
+    for t in (block_table, row_seq, row_pos):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("block_table, row_seq, row_pos must be contiguous int32")
+    n_rows = latent.shape[0]
+    if latent.stride(-1) != 1 or (rope is not None and rope.stride(-1) != 1):
+        raise ValueError("latent/rope rows must be contiguous")
+    if rope is not None and rope.dtype != latent.dtype:
+        raise ValueError("latent and rope must share a dtype")
+    batch = block_table.shape[0] if batch is None else batch
+    _check("tpla_append_kv",
+           lib().tpla_append_kv(cache.data_ptr(), _dt(cache), num_blocks, bs, d_s, d_r,
+                                block_table.data_ptr(), block_table.shape[1], batch,
+                                row_seq.data_ptr(), row_pos.data_ptr(), n_rows,
+                                latent.data_ptr(), latent.stride(0) if n_rows > 1 else d_s,
+                                None if rope is None else rope.data_ptr(),
+                                0 if rope is None else (rope.stride(0) if n_rows > 1 else d_r),
+                                _dt(latent), _stream(cache)))
+
+
+def make_decode_args(q_latent: torch.Tensor, q_rope: Optional[torch.Tensor], cache: torch.Tensor,
+                     block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                     max_seq_len: int, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                     num_splits: int = 0) -> DecodeArgs:
+    if q_rope is not None and q_rope.shape[-1] == 0:
+        q_rope = None
+    B, H, d_s = q_latent.shape
+    d_r = 0 if q_rope is None else q_rope.shape[-1]
+    num_blocks, bs, width = cache.shape
+    if width != d_s + d_r:
+        raise ValueError(f"cache row width {width} != d_s + d_r = {d_s + d_r}")
+    if q_latent.stride(-1) != 1 or (q_rope is not None and q_rope.stride(-1) != 1):
+        raise ValueError("query rows must be contiguous in their last dimension")
+    if out.shape != (B, H, d_s) or out.stride(-1) != 1:
+        raise ValueError("out must be [batch, heads, d_s] with a contiguous last dimension")
+    if lse is not None and (lse.shape != (B, H) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 [batch, heads]")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if not (block_table.is_contiguous() and seq_lens.is_contiguous()):
+        raise ValueError("block_table and seq_lens must be contiguous")
+    if q_rope is not None and q_rope.dtype != q_latent.dtype:
+        raise ValueError("q_latent and q_rope must share a dtype")
+    if cache.dtype != q_latent.dtype:
+        raise ValueError("query and cache must share a dtype")
+    a = DecodeArgs()
+    a.batch, a.heads, a.d_s, a.d_r = B, H, d_s, d_r
+    a.block_size, a.num_blocks, a.max_blocks_per_seq = bs, num_blocks, block_table.shape[1]
+    a.max_seq_len = int(max_seq_len)
+    a.dtype = _dt(q_latent)
+    a.scale = float(scale)
+    a.q_latent = q_latent.data_ptr()
+    a.q_latent_stride_b, a.q_latent_stride_h = q_latent.stride(0), q_latent.stride(1)
+    if q_rope is not None:
+        a.q_rope = q_rope.data_ptr()
+        a.q_rope_stride_b, a.q_rope_stride_h = q_rope.stride(0), q_rope.stride(1)
+    else:
+        a.q_rope, a.q_rope_stride_b, a.q_rope_stride_h = None, 0, 0
+    a.cache = cache.data_ptr()
+    a.block_table = block_table.data_ptr()
+    a.seq_lens = seq_lens.data_ptr()
+    a.out = out.data_ptr()
+    a.out_dtype = _dt(out)
+    a.out_stride_b, a.out_stride_h = out.stride(0), out.stride(1)
+    a.lse = None if lse is None else lse.data_ptr()
+    a.num_splits = int(num_splits)
+    return a
+
+
+def decode_workspace_size(args: DecodeArgs) -> int:
+    n = ctypes.c_size_t(0)
+    _check("tpla_decode_workspace_size", lib().tpla_decode_workspace_size(ctypes.byref(args),
+                                                                          ctypes.byref(n)))
+    return n.value
+
+
+def decode_shard(q_latent: torch.Tensor, q_rope: Optional[torch.Tensor], cache: torch.Tensor,
+                 block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                 max_seq_len: int, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, num_splits: int = 0,
+                 workspace: Optional[torch.Tensor] = None,
+                 out_dtype: torch.dtype = torch.float32):
+    """One shard's decode step.  Returns (out [B, H, d_s], lse [B, H] or None)."""
+    _gpu(q_latent, q_rope, cache, block_table, seq_lens, out, lse, workspace)
+    B, H, d_s = q_latent.shape
+    if out is None:
+        out = torch.empty((B, H, d_s), dtype=out_dtype, device=q_latent.device)
+    args = make_decode_args(q_latent, q_rope, cache, block_table, seq_lens, scale, max_seq_len,
+                            out, lse, num_splits)
+    need = decode_workspace_size(args)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_latent.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("tpla_decode_shard", lib().tpla_decode_shard(ctypes.byref(args), workspace.data_ptr(),
+                                                        nbytes, _stream(q_latent)))
+    return out, lse
+
+
+def combine_shards(partials: Sequence[torch.Tensor], out: Optional[torch.Tensor] = None,
+                   out_dtype: Optional[torch.dtype] = None, accumulate: bool = False) -> torch.Tensor:
+    """out[b, h, g*d_s:(g+1)*d_s] (+)= partials[g][b, h, :]."""
+    _gpu(*partials, out)
+    tp = len(partials)
+    B, H, d_s = partials[0].shape
+    for p in partials:
+        if p.shape != (B, H, d_s) or not p.is_contiguous() or p.dtype != partials[0].dtype:
+            raise ValueError("partials must be contiguous [batch, heads, d_s] of one dtype")
+    if out is None:
+        out = torch.empty((B, H, tp * d_s), dtype=out_dtype or partials[0].dtype,
+                          device=partials[0].device)
+    if out.shape != (B, H, tp * d_s) or not out.is_contiguous():
+        raise ValueError("out must be contiguous [batch, heads, tp*d_s]")
+    ptrs = (ctypes.c_void_p * tp)(*[p.data_ptr() for p in partials])
+    _check("tpla_combine_shards",
+           lib().tpla_combine_shards(ptrs, _dt(partials[0]), tp, B, H, d_s, out.data_ptr(),
+                                     _dt(out), int(accumulate), _stream(out)))
+    return out
+
+
+def version() -> int:
+    return int(lib().tpla_version())
+
+
+def default_scale(d_s_full: int, d_r: int) -> float:
+    return 1.0 / math.sqrt(d_s_full + d_r)

@@ -1,0 +1,148 @@
+"""libtpla.so on the CPU: it loads, exports what include/tpla.h declares, and
+rejects bad host arguments before touching the GPU (no compute calls)."""
+
+import ctypes
+import os
+
+import pytest
+
+from tensor_latent_decode_amd import tpla
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tpla.LIB_PATH),
+                                reason="libtpla.so not built (run __graft_entry__.build())")
+
+FAKE = 0x10000   # never dereferenced: every call below fails its host checks first
+
+
+def test_exports_every_declared_function():
+    names = tpla.header_functions()
+    assert {"tpla_hadamard_latent", "tpla_append_kv", "tpla_decode_workspace_size",
+            "tpla_decode_shard", "tpla_combine_shards", "tpla_status_string",
+            "tpla_last_error", "tpla_version"} <= set(names)
+    raw = ctypes.CDLL(tpla.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_status_strings():
+    L = tpla.lib()
+    assert tpla.version() == 100
+    for code in range(8):
+        assert L.tpla_status_string(code)
+    assert L.tpla_status_string(99) == b"unknown status"
+
+
+def _fails(code, expected):
+    assert code == expected, (code, tpla.lib().tpla_last_error())
+    assert tpla.lib().tpla_last_error() != b""
+
+
+def test_hadamard_argument_checks():
+    L = tpla.lib()
+    _fails(L.tpla_hadamard_latent(FAKE, 0, 12, FAKE, 0, 12, 4, 12, None), 2)    # n not 2^k
+    _fails(L.tpla_hadamard_latent(FAKE, 0, 8192, FAKE, 0, 8192, 4, 8192, None), 2)
+    _fails(L.tpla_hadamard_latent(FAKE, 5, 16, FAKE, 0, 16, 4, 16, None), 4)    # dtype
+    _fails(L.tpla_hadamard_latent(FAKE, 0, 8, FAKE, 0, 16, 4, 16, None), 2)     # stride < n
+    _fails(L.tpla_hadamard_latent(None, 0, 16, FAKE, 0, 16, 4, 16, None), 1)
+    _fails(L.tpla_hadamard_latent(FAKE, 0, 16, FAKE, 0, 16, -1, 16, None), 2)
+    assert L.tpla_hadamard_latent(None, 0, 16, None, 0, 16, 0, 16, None) == 0   # no rows
+
+
+def test_append_argument_checks():
+    L = tpla.lib()
+    base = [FAKE, 1, 10, 64, 256, 64, FAKE, 4, 2, FAKE, FAKE, 3, FAKE, 512, FAKE, 64, 1, None]
+    args = list(base)
+    args[1] = 7
+    _fails(L.tpla_append_kv(*args), 4)
+    args = list(base)
+    args[3] = 0
+    _fails(L.tpla_append_kv(*args), 2)
+    args = list(base)
+    args[13] = 100                          # latent row stride < d_s
+    _fails(L.tpla_append_kv(*args), 2)
+    args = list(base)
+    args[0] = None
+    _fails(L.tpla_append_kv(*args), 1)
+    args = list(base)
+    args[14] = None                         # rope NULL with d_r > 0
+    _fails(L.tpla_append_kv(*args), 1)
+    args = list(base)
+    args[11] = 0
+    args[0] = None
+    assert L.tpla_append_kv(*args) == 0     # zero rows is a no-op
+
+
+def _args(**kw):
+    a = tpla.DecodeArgs()
+    a.batch, a.heads, a.d_s, a.d_r = 2, 128, 256, 64
+    a.block_size, a.num_blocks, a.max_blocks_per_seq, a.max_seq_len = 64, 100, 50, 3200
+    a.dtype, a.scale = 1, 0.07
+    a.q_latent, a.q_latent_stride_b, a.q_latent_stride_h = FAKE, 128 * 512, 512
+    a.q_rope, a.q_rope_stride_b, a.q_rope_stride_h = FAKE, 128 * 64, 64
+    a.cache, a.block_table, a.seq_lens = FAKE, FAKE, FAKE
+    a.out, a.out_dtype, a.out_stride_b, a.out_stride_h = FAKE, 0, 128 * 256, 256
+    a.lse, a.num_splits = None, 4
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_workspace_size_with_fixed_splits():
+    # 3200 tokens in 4 splits -> 50 tiles, 13 tiles (832 tokens) per split -> 4 splits
+    n = ctypes.c_size_t()
+    L = tpla.lib()
+    assert L.tpla_decode_workspace_size(ctypes.byref(_args()), ctypes.byref(n)) == 0
+    rows = 4 * 2 * 128
+    o = (rows * 256 * 4 + 255) // 256 * 256
+    lse = (rows * 4 + 255) // 256 * 256
+    assert n.value == o + lse
+    # more splits than tiles are clamped to one per 64-token tile
+    assert L.tpla_decode_workspace_size(ctypes.byref(_args(num_splits=1000)), ctypes.byref(n)) == 0
+    assert n.value == (50 * 2 * 128 * 256 * 4 + 255) // 256 * 256 + (50 * 2 * 128 * 4 + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), 2), (dict(heads=0), 2), (dict(d_r=-1), 2), (dict(block_size=0), 2),
+    (dict(max_seq_len=50 * 64 + 1), 2), (dict(dtype=3), 4), (dict(out_dtype=9), 4),
+    (dict(q_latent=None), 1), (dict(cache=None), 1), (dict(block_table=None), 1),
+    (dict(seq_lens=None), 1), (dict(out=None), 1), (dict(q_rope=None), 1),
+    (dict(num_splits=-1), 2), (dict(q_latent_stride_h=100), 2), (dict(out_stride_h=10), 2),
+    (dict(scale=float("nan")), 2), (dict(scale=float("inf")), 2),
+    (dict(dtype=0, d_s=2048, d_r=64, q_latent_stride_h=2048, q_latent_stride_b=128 * 2048,
+          out_stride_h=2048, out_stride_b=128 * 2048), 5),
+])
+def test_decode_argument_checks(kw, code):
+    n = ctypes.c_size_t()
+    L = tpla.lib()
+    _fails(L.tpla_decode_workspace_size(ctypes.byref(_args(**kw)), ctypes.byref(n)), code)
+    _fails(L.tpla_decode_shard(ctypes.byref(_args(**kw)), FAKE, 1 << 40, None), code)
+
+
+def test_decode_null_args_and_workspace_checks():
+    L = tpla.lib()
+    n = ctypes.c_size_t()
+    _fails(L.tpla_decode_workspace_size(None, ctypes.byref(n)), 1)
+    _fails(L.tpla_decode_workspace_size(ctypes.byref(_args()), None), 1)
+    _fails(L.tpla_decode_shard(None, FAKE, 1 << 30, None), 1)
+    _fails(L.tpla_decode_shard(ctypes.byref(_args()), None, 1 << 30, None), 6)
+    _fails(L.tpla_decode_shard(ctypes.byref(_args()), FAKE, 16, None), 6)
+    _fails(L.tpla_decode_shard(ctypes.byref(_args()), FAKE + 4, 1 << 30, None), 3)
+
+
+def test_combine_argument_checks():
+    L = tpla.lib()
+    ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    _fails(L.tpla_combine_shards(ptrs, 0, 0, 1, 1, 8, FAKE, 0, 0, None), 2)
+    _fails(L.tpla_combine_shards(ptrs, 0, 17, 1, 1, 8, FAKE, 0, 0, None), 2)
+    _fails(L.tpla_combine_shards(ptrs, 2, 2, 1, 1, 8, FAKE, 0, 0, None), 4)
+    _fails(L.tpla_combine_shards(None, 0, 2, 1, 1, 8, FAKE, 0, 0, None), 1)
+    _fails(L.tpla_combine_shards(ptrs, 0, 2, 1, 1, 8, None, 0, 0, None), 1)
+    nullp = (ctypes.c_void_p * 2)(FAKE, None)
+    _fails(L.tpla_combine_shards(nullp, 0, 2, 1, 1, 8, FAKE, 0, 0, None), 1)
+    _fails(L.tpla_combine_shards(ptrs, 0, 2, 0, 1, 8, FAKE, 0, 0, None), 2)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        tpla.hadamard_latent(torch.zeros(4, 16))

@@ -1,0 +1,334 @@
+"""GPU parity of every libtpla entry point against the fp64 oracle.
+
+Bars: integer/index work (append, combine placement) bit-exact; floating
+point max|gpu - oracle| / max|oracle| <= 5e-3 for bf16 inputs with float32
+accumulation (1e-5 for float32 inputs).  Caches start NaN-filled, so a
+kernel that reads a row it was not given produces NaN and fails.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tensor_latent_decode_amd import tpla
+from tensor_latent_decode_amd.inputs import CONFIGS, make_case
+from tpla_testlib import (TOL_BF16, TOL_FP32, GpuCase, as_f64, dev, host_bits, host_f64,
+                          oracle_step, rel_err)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# --------------------------------------------------------------------------
+# Hadamard
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 4, 16, 64, 128, 512, 1024, 4096])
+@pytest.mark.parametrize("dts", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16")])
+def test_hadamard_parity(n, dts):
+    rng = np.random.default_rng(n)
+    rows = 37
+    x32 = rng.standard_normal((rows, n)).astype(np.float32)
+    tin = torch.bfloat16 if dts[0] == "bf16" else torch.float32
+    tout = torch.bfloat16 if dts[1] == "bf16" else torch.float32
+    x = torch.from_numpy(x32).cuda().to(tin)
+    y = tpla.hadamard_latent(x, out_dtype=tout)
+    ref = oracle.fwht(host_f64(x))
+    tol = TOL_BF16 if "bf16" in dts[1] else TOL_FP32
+    assert rel_err(host_f64(y), ref) <= tol
+
+
+def test_hadamard_inplace_strided_rows_and_self_inverse():
+    rng = np.random.default_rng(2)
+    base = torch.from_numpy(rng.standard_normal((5, 7, 512)).astype(np.float32)).cuda()
+    x = base[:, :, :]                       # [5, 7, 512] rows of a larger buffer
+    big = torch.zeros((35, 1024), device="cuda")
+    big[:, :512] = x.reshape(35, 512)
+    view = big[:, :512]                     # row stride 1024
+    ref = oracle.fwht(host_f64(view))
+    tpla.hadamard_latent(view, out=view)
+    assert rel_err(host_f64(view), ref) <= TOL_FP32
+    assert torch.all(big[:, 512:] == 0)
+    tpla.hadamard_latent(view, out=view)
+    assert rel_err(host_f64(view), host_f64(x.reshape(35, 512))) <= 1e-5
+
+
+# --------------------------------------------------------------------------
+# Paged append (bit-exact)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,bs", [("tiny_fp32", 16), ("tiny_fp32", 64), ("dsv3_4k", 64),
+                                    ("dsv3_4k", 16), ("kimi_k2_32k", 64)])
+def test_append_bit_exact(cfg, bs):
+    case = make_case(CONFIGS[cfg], batch=3, ctx=(30, 200), block_size=bs, seed=7,
+                     heads=min(CONFIGS[cfg].heads, 32))
+    g_case = GpuCase(case)
+    d_s = case.cfg.d_s
+    for g in range(case.cfg.tp):
+        cache = g_case.prefill(g, d_s)
+        tpla.append_kv(cache, g_case.bt, g_case.new_seq, g_case.new_pos,
+                       g_case.new_latent[:, g * d_s:(g + 1) * d_s], g_case.new_rope)
+        torch.cuda.synchronize()
+        ref = np.full(tuple(cache.shape), 0xFFFF if case.cfg.dtype == "bf16" else np.nan,
+                      dtype=np.uint16 if case.cfg.dtype == "bf16" else np.float32)
+        oracle.paged_append(ref, case.block_table, bs, case.hist_seq, case.hist_pos,
+                            case.hist_latent[:, g * d_s:(g + 1) * d_s], case.hist_rope)
+        oracle.paged_append(ref, case.block_table, bs, np.arange(3), case.new_pos,
+                            case.new_latent[:, g * d_s:(g + 1) * d_s], case.new_rope)
+        got = host_bits(cache)
+        np.testing.assert_array_equal(got.view(np.uint32 if got.dtype == np.float32 else np.uint16),
+                                      ref.view(np.uint32 if ref.dtype == np.float32 else np.uint16))
+
+
+def test_append_fp32_source_rounds_to_bf16_nearest_even():
+    case = make_case(CONFIGS["dsv3_4k"], batch=2, ctx=(10, 80), seed=8, heads=32)
+    g_case = GpuCase(case)
+    rng = np.random.default_rng(9)
+    src = rng.standard_normal((2, 256)).astype(np.float32)
+    src[0, :8] = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0, -0.0, 3e38,
+                           1e-40, 2 ** -8], np.float32)     # ties, signed zero, big, subnormal
+    rope = rng.standard_normal((2, 64)).astype(np.float32)
+    cache = g_case.prefill(0, 256)
+    tpla.append_kv(cache, g_case.bt, g_case.new_seq, g_case.new_pos, dev(src), dev(rope))
+    ref = np.full(tuple(cache.shape), 0xFFFF, np.uint16)
+    oracle.paged_append(ref, case.block_table, 64, case.hist_seq, case.hist_pos,
+                        case.hist_latent[:, :256], case.hist_rope)
+    oracle.paged_append(ref, case.block_table, 64, np.arange(2), case.new_pos, src, rope)
+    np.testing.assert_array_equal(host_bits(cache), ref)
+
+
+def test_append_skips_out_of_range_rows():
+    case = make_case(CONFIGS["dsv3_4k"], batch=2, ctx=(10, 80), seed=10, heads=32)
+    g_case = GpuCase(case)
+    cache = g_case.prefill(0, 256)
+    before = host_bits(cache).copy()
+    bad_seq = torch.tensor([-1, 2, 0, 1], dtype=torch.int32, device="cuda")
+    bad_pos = torch.tensor([0, 0, -5, case.max_blocks * 64], dtype=torch.int32, device="cuda")
+    lat = torch.ones((4, 256), dtype=torch.bfloat16, device="cuda")
+    rope = torch.ones((4, 64), dtype=torch.bfloat16, device="cuda")
+    tpla.append_kv(cache, g_case.bt, bad_seq, bad_pos, lat, rope)
+    bt = g_case.bt.clone()
+    bt[0, 0] = case.num_blocks + 5           # invalid block id
+    tpla.append_kv(cache, bt, torch.tensor([0], dtype=torch.int32, device="cuda"),
+                   torch.tensor([0], dtype=torch.int32, device="cuda"), lat[:1], rope[:1])
+    np.testing.assert_array_equal(host_bits(cache), before)
+
+
+# --------------------------------------------------------------------------
+# Combine (bit-exact placement)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tp", [1, 2, 4])
+@pytest.mark.parametrize("out_dt", [torch.float32, torch.bfloat16])
+def test_combine_bit_exact(tp, out_dt):
+    rng = np.random.default_rng(tp)
+    parts = [rng.standard_normal((3, 5, 64)).astype(np.float32) for _ in range(tp)]
+    parts[0][0, 0, :3] = [-0.0, 0.0, 1 + 2 ** -8]
+    out = tpla.combine_shards([dev(p) for p in parts], out_dtype=out_dt)
+    ref = oracle.combine_shards([p.astype(np.float64) for p in parts]).astype(np.float32)
+    if out_dt == torch.float32:
+        want = np.concatenate(parts, axis=-1)
+        np.testing.assert_array_equal(host_bits(out).view(np.uint32), want.view(np.uint32))
+        np.testing.assert_array_equal(host_bits(out), ref)
+    else:
+        # values, not bits: the oracle's zero-padded sum turns -0.0 into +0.0
+        np.testing.assert_array_equal(oracle.bf16_bits_to_f64(host_bits(out)),
+                                      oracle.bf16_bits_to_f64(oracle.f32_to_bf16_bits(ref)))
+
+
+def test_combine_accumulate():
+    rng = np.random.default_rng(3)
+    parts = [rng.standard_normal((2, 3, 32)).astype(np.float32) for _ in range(2)]
+    base = rng.standard_normal((2, 3, 64)).astype(np.float32)
+    out = dev(base)
+    tpla.combine_shards([dev(p) for p in parts], out=out, accumulate=True)
+    ref = base.astype(np.float64) + oracle.combine_shards([p.astype(np.float64) for p in parts])
+    assert rel_err(host_f64(out), ref) <= 1e-6
+
+
+# --------------------------------------------------------------------------
+# Decode: tiny float32 TPLA, both shards, Hadamard on and off (full step)
+# --------------------------------------------------------------------------
+
+def run_step(gc: GpuCase, hadamard: bool, num_splits: int = 0, out_dtype=torch.float32):
+    """The library's whole decode step on one GPU: rotate query and new latent,
+    then for every shard append the new row and decode; combine."""
+    case = gc.case
+    cfg = case.cfg
+    d_s = cfg.d_s
+    q = tpla.hadamard_latent(gc.q_latent) if hadamard else gc.q_latent
+    new = tpla.hadamard_latent(gc.new_latent) if hadamard else gc.new_latent
+    outs, lses, caches = [], [], []
+    for g in range(cfg.tp):
+        cache = gc.prefill(g, d_s)
+        tpla.append_kv(cache, gc.bt, gc.new_seq, gc.new_pos, new[:, g * d_s:(g + 1) * d_s],
+                       gc.new_rope)
+        lse = torch.empty((cfg.batch, cfg.heads), dtype=torch.float32, device="cuda")
+        o, _ = tpla.decode_shard(q[:, :, g * d_s:(g + 1) * d_s], gc.q_rope, cache, gc.bt,
+                                 gc.seq_lens, cfg.scale, int(case.seq_lens.max()), lse=lse,
+                                 num_splits=num_splits, out_dtype=out_dtype)
+        outs.append(o)
+        lses.append(lse)
+        caches.append(cache)
+    combined = tpla.combine_shards([o.float() for o in outs])
+    torch.cuda.synchronize()
+    return combined, outs, lses
+
+
+@pytest.mark.parametrize("hadamard", [False, True])
+@pytest.mark.parametrize("bs", [64, 16])
+def test_tiny_fp32_full_step(hadamard, bs):
+    case = make_case(CONFIGS["tiny_fp32"], block_size=bs)
+    gc = GpuCase(case)
+    combined, outs, lses = run_step(gc, hadamard)
+    ref, parts = oracle_step(case, 0, case.cfg.tp, hadamard)
+    assert rel_err(host_f64(combined)[0], ref) <= TOL_FP32
+    for g, (o, l) in enumerate(parts):
+        assert rel_err(host_f64(outs[g])[0], o) <= TOL_FP32
+        assert np.max(np.abs(host_f64(lses[g])[0] - l)) <= 1e-4
+
+
+def test_tiny_fp32_hadamard_unrotate_matches_oracle():
+    case = make_case(CONFIGS["tiny_fp32"])
+    gc = GpuCase(case)
+    combined, _, _ = run_step(gc, True)
+    back = tpla.hadamard_latent(combined)
+    ref, _ = oracle_step(case, 0, 2, True)
+    assert rel_err(host_f64(back)[0], oracle.fwht(ref)) <= TOL_FP32
+
+
+# --------------------------------------------------------------------------
+# Decode: bf16 matrix-core kernel over shapes, tails, block sizes and splits
+# --------------------------------------------------------------------------
+
+SHAPES = [  # (heads, d_c, tp, d_r)
+    (128, 512, 2, 64),      # DeepSeek-V3 shard
+    (64, 512, 4, 64),       # Kimi-K2 shard
+    (32, 128, 2, 64),
+    (128, 256, 2, 0),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("bs", [64, 16, 128])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_decode_bf16_ragged_parity(shape, bs, splits):
+    H, d_c, tp, d_r = shape
+    cfg = CONFIGS["dsv3_4k"]
+    from dataclasses import replace
+    cfg = replace(cfg, heads=H, d_c=d_c, tp=tp, d_r=d_r, scale=1 / math.sqrt(192.0))
+    case = make_case(cfg, batch=6, ctx=(1, 700), block_size=bs, seed=31 + H + bs)
+    gc = GpuCase(case)
+    combined, outs, lses = run_step(gc, hadamard=False, num_splits=splits)
+    got = host_f64(combined)
+    for b in range(cfg.batch):
+        ref, parts = oracle_step(case, b, tp, hadamard=False)
+        assert rel_err(got[b], ref) <= TOL_BF16, (b, int(case.seq_lens[b]))
+        for g, (o, l) in enumerate(parts):
+            assert np.max(np.abs(host_f64(lses[g])[b] - l)) <= 2e-2
+
+
+@pytest.mark.parametrize("lens", [[1, 2, 63, 64], [65, 127, 128, 129], [4096, 1, 1000, 3]])
+def test_decode_bf16_edge_lengths(lens):
+    cases = [make_case(CONFIGS["dsv3_4k"], batch=1, ctx=L, seed=41 + i)
+             for i, L in enumerate(lens)]
+    for c in cases:
+        gc = GpuCase(c)
+        combined, _, _ = run_step(gc, hadamard=True)
+        ref, _ = oracle_step(c, 0, 2, hadamard=True)
+        assert rel_err(host_f64(combined)[0], ref) <= TOL_BF16, int(c.seq_lens[0])
+
+
+def test_decode_generic_bf16_odd_shape():
+    from dataclasses import replace
+    cfg = replace(CONFIGS["dsv3_4k"], heads=5, d_c=80, tp=2, d_r=8, scale=0.2)
+    case = make_case(cfg, batch=3, ctx=(1, 300), seed=50, block_size=32)
+    gc = GpuCase(case)
+    combined, _, _ = run_step(gc, hadamard=False, num_splits=2)
+    for b in range(3):
+        ref, _ = oracle_step(case, b, 2, hadamard=False)
+        assert rel_err(host_f64(combined)[b], ref) <= TOL_BF16
+
+
+def test_decode_empty_sequence_gives_zero_and_minus_inf():
+    case = make_case(CONFIGS["dsv3_4k"], batch=2, ctx=100, seed=60)
+    gc = GpuCase(case)
+    cache = gc.prefill(0, 256)
+    lens = torch.tensor([0, 99], dtype=torch.int32, device="cuda")
+    lse = torch.empty((2, 128), dtype=torch.float32, device="cuda")
+    o, _ = tpla.decode_shard(gc.q_latent[:, :, :256], gc.q_rope, cache, gc.bt, lens,
+                             case.cfg.scale, 100, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    ref, parts = oracle_step(case, 1, 2, hadamard=False, with_new=False, q_is_rotated=True)
+    assert rel_err(host_f64(o)[1], parts[0][0]) <= TOL_BF16
+
+
+def test_decode_bf16_output_and_determinism():
+    case = make_case(CONFIGS["dsv3_4k"], batch=2, ctx=(500, 3000), seed=61)
+    gc = GpuCase(case)
+    cache = gc.prefill(0, 256)
+    lens = gc.hist_lens
+    maxlen = int(case.seq_lens.max())
+    a, _ = tpla.decode_shard(gc.q_latent[:, :, :256], gc.q_rope, cache, gc.bt, lens,
+                             case.cfg.scale, maxlen, out_dtype=torch.bfloat16)
+    b, _ = tpla.decode_shard(gc.q_latent[:, :, :256], gc.q_rope, cache, gc.bt, lens,
+                             case.cfg.scale, maxlen, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for s in range(2):
+        _, parts = oracle_step(case, s, 2, hadamard=False, with_new=False, q_is_rotated=True)
+        assert rel_err(host_f64(a)[s], parts[0][0]) <= TOL_BF16
+
+
+# --------------------------------------------------------------------------
+# The workloads at their real sizes (sampled sequences)
+# --------------------------------------------------------------------------
+
+def test_dsv3_4k_full():
+    case = make_case(CONFIGS["dsv3_4k"])
+    gc = GpuCase(case)
+    combined, outs, _ = run_step(gc, hadamard=True)
+    ref, parts = oracle_step(case, 0, 2, hadamard=True)
+    assert rel_err(host_f64(combined)[0], ref) <= TOL_BF16
+    for g in range(2):
+        assert rel_err(host_f64(outs[g])[0], parts[g][0]) <= TOL_BF16
+
+
+@pytest.mark.parametrize("name", ["dsv3_32k", "kimi_k2_32k"])
+def test_32k_shard_sampled(name):
+    """One shard (g = 0) at its real shape, automatic splits as the bench runs it."""
+    case = make_case(CONFIGS[name])
+    gc = GpuCase(case)
+    cfg = case.cfg
+    d_s = cfg.d_s
+    q = tpla.hadamard_latent(gc.q_latent)
+    new = tpla.hadamard_latent(gc.new_latent)
+    cache = gc.prefill(0, d_s)
+    tpla.append_kv(cache, gc.bt, gc.new_seq, gc.new_pos, new[:, :d_s], gc.new_rope)
+    o, _ = tpla.decode_shard(q[:, :, :d_s], gc.q_rope, cache, gc.bt, gc.seq_lens, cfg.scale,
+                             int(case.seq_lens.max()))
+    torch.cuda.synchronize()
+    got = host_f64(o)
+    for b in (0, cfg.batch // 2, cfg.batch - 1):
+        _, parts = oracle_step(case, b, cfg.tp, hadamard=True)
+        assert rel_err(got[b], parts[0][0]) <= TOL_BF16, b
+
+
+def test_ragged_tp2_full_step_sampled():
+    case = make_case(CONFIGS["ragged_tp2"])
+    gc = GpuCase(case)
+    combined, _, _ = run_step(gc, hadamard=True)
+    got = host_f64(combined)
+    order = np.argsort(case.seq_lens)
+    for b in (int(order[0]), int(order[-1]), 7):
+        ref, _ = oracle_step(case, b, 2, hadamard=True)
+        assert rel_err(got[b], ref) <= TOL_BF16, (b, int(case.seq_lens[b]))
