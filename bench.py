@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of one TPLA decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload dsv3_32k]
+
+A step is the whole decode hot path over one batch, with every input already
+resident in HBM: rotate the absorbed query and the new token's latent
+(tpla_hadamard_latent), append the new row to the shard cache
+(tpla_append_kv), decode the shard (tpla_decode_shard: split-K attention and
+log-sum-exp merge) and combine the shard outputs (tpla_combine_shards).
+The default workload is the DeepSeek-V3-shaped shard at 32K context
+(B=16, H=128, d_c=512 split TP=2 -> d_s=256, d_r=64, paged blocks of 64 with
+a permuted block table); `--workload ragged_tp2` runs both shards of the
+ragged TP=2 step in turn.
+
+Steps are replayed from HIP graphs (one per cache replica).  Replicas rotate
+so that the caches read by consecutive steps together exceed the 256 MB
+Infinity Cache (the next layer's cache would evict it in a real model).
+
+Prints one JSON line.  `value` is the latent-cache bytes the step streams
+(sum_b L_b * (d_s + d_r) * 2 per shard) divided by the step time, in GB/s.
+`roofline` gives the decode kernel alone, timed with HIP events in a loop of
+back-to-back launches on its own stream right after the timed steps;
+`cpu_baseline` times the fp64 oracle on the host over a bounded sample.
+
+`--mode copy` runs a plain 1 GiB device copy (for calibrating rocprofv3
+FETCH_SIZE/WRITE_SIZE counters); `--mode decode` runs only decode launches.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TPLA decode: latent-cache GB/s (% HBM peak) and decode tokens/s at 32K ctx"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
+MALL_BYTES = 256 * 2 ** 20      # Infinity Cache
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_32k",
+                    choices=["dsv3_32k", "kimi_k2_32k", "ragged_tp2", "dsv3_4k"])
+    ap.add_argument("--mode", default="step", choices=["step", "decode", "copy"])
+    ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = auto)")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--decode-launches", type=int, default=40)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the oracle's host timing (0 disables it)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tensor_latent_decode_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.startswith("decode_") or name == "tpla_api.hip":
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per decode launch from committed rocprofv3 counters, if they
+    were taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sha") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run_copy(torch, steps):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "ms_per_copy": ms, "copy_GBps": 2 * n / ms / 1e6}), flush=True)
+
+
+def cpu_baseline(case, seconds: float):
+    """The fp64 oracle over whole sequences of the same workload, on the host."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:           # pragma: no cover - threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    cfg = case.cfg
+    d_s, tp = cfg.d_s, cfg.tp
+    shards = list(range(tp)) if cfg.name == "ragged_tp2" else [0]
+    bs = cfg.block_size
+    f64 = oracle.bf16_bits_to_f64
+    starts = np.concatenate([[0], np.cumsum(case.seq_lens - 1)])
+    done_bytes = 0
+    done_seqs = 0
+    elapsed = 0.0
+    for b in range(cfg.batch):
+        n = int(case.seq_lens[b]) - 1
+        rows = slice(int(starts[b]), int(starts[b]) + n)
+        # this sequence's paged cache per shard (history rows: set-up, not timed)
+        caches = []
+        for g in shards:
+            cache = np.zeros((case.num_blocks, bs, d_s + cfg.d_r), np.uint16)
+            oracle.paged_append(cache, case.block_table, bs, case.hist_seq[rows],
+                                case.hist_pos[rows], case.hist_latent[rows, g * d_s:(g + 1) * d_s],
+                                case.hist_rope[rows])
+            caches.append(cache)
+        t0 = time.perf_counter()
+        q = oracle.fwht(f64(case.q_latent[b]))
+        new = oracle.f32_to_bf16_bits(oracle.fwht(f64(case.new_latent[b])[None]).astype(np.float32))
+        outs = []
+        for g, cache in zip(shards, caches):
+            oracle.paged_append(cache, case.block_table, bs, np.array([b]), case.new_pos[b:b + 1],
+                                new[:, g * d_s:(g + 1) * d_s], case.new_rope[b:b + 1])
+            o, _ = oracle.tpla_decode_paged(
+                oracle.shard_slice(q, g, tp)[None], f64(case.q_rope[b])[None], cache,
+                case.block_table[b:b + 1], case.seq_lens[b:b + 1], bs, d_s, cfg.scale)
+            outs.append(o)
+        oracle.combine_shards(outs)
+        elapsed += time.perf_counter() - t0
+        done_bytes += int(case.seq_lens[b]) * (d_s + cfg.d_r) * 2 * len(shards)
+        done_seqs += 1
+        if elapsed >= seconds:
+            break
+    return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done_seqs} of {cfg.batch} sequences of the same workload (whole step "
+                      f"per sequence: rotate, append, paged gather + fp64 attention per shard, "
+                      f"combine), {elapsed:.1f} s on the host; tokens/s "
+                      f"{done_seqs / elapsed:.3g}"}
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): TPLA shards would sit on separate GPUs joined by an RCCL "
+              "collective, which this build does not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from tensor_latent_decode_amd import tpla
+    from tensor_latent_decode_amd.inputs import CONFIGS, make_case
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    if args.mode == "copy":
+        run_copy(torch, max(args.steps, 1))
+        return
+
+    t_setup = time.perf_counter()
+    case = make_case(CONFIGS[args.workload])
+    cfg = case.cfg
+    B, H, d_c, d_s, d_r, tp = cfg.batch, cfg.heads, cfg.d_c, cfg.d_s, cfg.d_r, cfg.tp
+    shards = list(range(tp)) if args.workload == "ragged_tp2" else [0]
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    bt, lens = dev(case.block_table), dev(case.seq_lens)
+    q_raw, q_rope = dev(case.q_latent), dev(case.q_rope)
+    new_raw, new_rope = dev(case.new_latent), dev(case.new_rope)
+    new_seq = torch.arange(B, dtype=torch.int32, device="cuda")
+    new_pos = dev(case.new_pos)
+    cache_bytes = int(case.num_blocks) * cfg.block_size * (d_s + d_r) * 2
+    step_cache_bytes = cache_bytes * len(shards)
+    replicas = args.replicas or max(2, -(-3 * MALL_BYTES // step_cache_bytes))
+    hist_lat, hist_rope = dev(case.hist_latent), dev(case.hist_rope)
+    hist_seq, hist_pos = dev(case.hist_seq), dev(case.hist_pos)
+    caches = []
+    for _ in range(replicas):
+        per = []
+        for g in shards:
+            c = torch.empty((case.num_blocks, cfg.block_size, d_s + d_r), dtype=torch.bfloat16,
+                            device="cuda")
+            tpla.append_kv(c, bt, hist_seq, hist_pos, hist_lat[:, g * d_s:(g + 1) * d_s], hist_rope)
+            per.append(c)
+        caches.append(per)
+    del hist_lat, hist_rope, hist_seq, hist_pos
+    maxlen = int(case.seq_lens.max())
+    q_rot = torch.empty((B, H, d_c), dtype=torch.bfloat16, device="cuda")
+    new_rot = torch.empty((B, d_c), dtype=torch.bfloat16, device="cuda")
+    outs = [torch.empty((B, H, d_s), dtype=torch.float32, device="cuda") for _ in shards]
+    lses = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in shards]
+    combined = torch.empty((B, H, len(shards) * d_s), dtype=torch.float32, device="cuda")
+    args0 = tpla.make_decode_args(q_rot[:, :, :d_s], q_rope, caches[0][0], bt, lens, cfg.scale,
+                                  maxlen, outs[0], lses[0], args.num_splits)
+    ws_bytes = tpla.decode_workspace_size(args0)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def decode(r, i, g):
+        tpla.decode_shard(q_rot[:, :, g * d_s:(g + 1) * d_s], q_rope, caches[r][i], bt, lens,
+                          cfg.scale, maxlen, out=outs[i], lse=lses[i], num_splits=args.num_splits,
+                          workspace=workspace)
+
+    def step(r):
+        tpla.hadamard_latent(q_raw, out=q_rot)
+        tpla.hadamard_latent(new_raw, out=new_rot)
+        for i, g in enumerate(shards):
+            tpla.append_kv(caches[r][i], bt, new_seq, new_pos, new_rot[:, g * d_s:(g + 1) * d_s],
+                           new_rope)
+            decode(r, i, g)
+        tpla.combine_shards(outs, out=combined)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for r in range(replicas):          # eager warm-up of every replica
+            step(r)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graphs = []
+    for r in range(replicas):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            step(r)
+        graphs.append(gr)
+    # graph of back-to-back decode launches (replicas rotating) for kernel timing
+    dec_graph = torch.cuda.CUDAGraph()
+    n_dec = max(args.decode_launches, replicas)
+    with torch.cuda.graph(dec_graph, stream=stream):
+        for k in range(n_dec):
+            decode(k % replicas, 0, shards[0])
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    if args.mode == "step" or args.mode == "decode":
+        for k in range(args.warmup):
+            graphs[k % replicas].replay()
+        torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    if args.mode == "decode":
+        # profiling aid: decode launches only
+        for _ in range(max(1, args.steps // n_dec)):
+            dec_graph.replay()
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "decode", "launches": n_dec * max(1, args.steps // n_dec)}))
+        return
+
+    torch.cuda.synchronize()
+    ev0.record()
+    for k in range(args.steps):
+        graphs[k % replicas].replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # decode kernel alone: back-to-back launches on the same stream
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    dec_graph.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        d0.record(stream)
+        reps = 3
+        for _ in range(reps):
+            dec_graph.replay()
+        d1.record(stream)
+    torch.cuda.synchronize()
+    ms_dec = d0.elapsed_time(d1) / (reps * n_dec)
+
+    lens_sum = int(np.sum(case.seq_lens.astype(np.int64)))
+    bytes_per_shard = lens_sum * (d_s + d_r) * 2
+    step_bytes = bytes_per_shard * len(shards)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = bytes_per_shard / (ms_dec * 1e-3) / 1e9
+    traffic = stored_traffic(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "heads": H, "d_c": d_c, "tp": tp,
+                   "shards_run": len(shards), "d_s": d_s, "d_r": d_r,
+                   "context": (list(cfg.ctx) if isinstance(cfg.ctx, tuple) else cfg.ctx),
+                   "tokens_attended": lens_sum, "block_size": cfg.block_size,
+                   "cache_replicas": replicas, "global_batch": B,
+                   "seq_len": maxlen},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "tpla_decode_shard (split-K attention + LSE merge)",
+                     "ms_per_launch": round(ms_dec, 5),
+                     "algorithmic_bytes_per_launch": bytes_per_shard},
+        "setup_s": round(setup_s, 1),
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,42 +15,60 @@
 namespace tpla {
 namespace {
 
-// One 64-lane wavefront per (b, h); lanes stride over d_s.
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t bh = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
-  if (bh >= static_cast<int64_t>(p.batch) * p.heads) return;
+// One thread per (b, h, 4 consecutive columns); a wavefront covers 256
+// columns of one or more (b, h) rows, so the lse reads are broadcasts and the
+// partial reads are contiguous float4 runs.  Workgroup n handles items
+// ((n % 8) * per_xcd + n / 8) * 256 ..., i.e. sequences are spread over the
+// XCDs in the same order as the split-K kernel placed them.
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_items, int per_xcd) {
+  const int n = blockIdx.x;
+  const int64_t wg = static_cast<int64_t>(n & 7) * per_xcd + (n >> 3);
+  const int64_t item = wg * 256 + threadIdx.x;
+  if (item >= n_items) return;
+  const int q4 = (p.d_s + 3) / 4;
+  const int64_t bh = item / q4;
+  const int col = static_cast<int>(item % q4) * 4;
+  const int ncol = min(4, p.d_s - col);
+  const bool vec = (p.d_s & 3) == 0;
   const int64_t stride_s = static_cast<int64_t>(p.batch) * p.heads;
   float mx = -INFINITY;
   for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.ws_lse[s * stride_s + bh]);
   const int b = static_cast<int>(bh / p.heads);
   const int h = static_cast<int>(bh % p.heads);
-  const int64_t obase = b * p.out_sb + h * p.out_sh;
-  if (mx == -INFINITY) {
-    for (int k = lane; k < p.d_s; k += 64) {
-      if (p.out_bf16) static_cast<uint16_t*>(p.out)[obase + k] = 0;
-      else static_cast<float*>(p.out)[obase + k] = 0.f;
-    }
-    if (p.lse != nullptr && lane == 0) p.lse[bh] = -INFINITY;
-    return;
-  }
-  float tot = 0.f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float l = p.ws_lse[s * stride_s + bh];
-    if (l != -INFINITY) tot += __expf(l - mx);
-  }
-  const float lse = mx + __logf(tot);
-  for (int k = lane; k < p.d_s; k += 64) {
-    float acc = 0.f;
+  const int64_t obase = b * p.out_sb + h * p.out_sh + col;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float lse = -INFINITY;
+  if (mx != -INFINITY) {
+    float tot = 0.f;
     for (int s = 0; s < p.splits; ++s) {
       const float l = p.ws_lse[s * stride_s + bh];
       if (l == -INFINITY) continue;
-      acc += __expf(l - lse) * p.ws_o[(s * stride_s + bh) * p.d_s + k];
+      const float w = __expf(l - mx);
+      tot += w;
+      const float* src = p.ws_o + (s * stride_s + bh) * p.d_s + col;
+      if (vec) {
+        const float4 o = *reinterpret_cast<const float4*>(src);
+        acc[0] += w * o.x;
+        acc[1] += w * o.y;
+        acc[2] += w * o.z;
+        acc[3] += w * o.w;
+      } else {
+        for (int i = 0; i < ncol; ++i) acc[i] += w * src[i];
+      }
     }
-    if (p.out_bf16) static_cast<uint16_t*>(p.out)[obase + k] = f32_to_bf16(acc);
-    else static_cast<float*>(p.out)[obase + k] = acc;
+    const float inv = 1.0f / tot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] *= inv;
+    lse = mx + __logf(tot);
   }
-  if (p.lse != nullptr && lane == 0) p.lse[bh] = lse;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i >= ncol) break;
+    if (kBf16Out) static_cast<uint16_t*>(p.out)[obase + i] = f32_to_bf16(acc[i]);
+    else static_cast<float*>(p.out)[obase + i] = acc[i];
+  }
+  if (p.lse != nullptr && col == 0) p.lse[bh] = lse;
 }
 
 template <typename TP, typename TO>
@@ -91,10 +109,16 @@ hipError_t launch_c(const PartPtrs& parts, int tp, int batch, int heads, int d_s
 }  // namespace
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
-  const int64_t waves = static_cast<int64_t>(p.batch) * p.heads;
-  const int64_t blocks = (waves + 3) / 4;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p);
+  const int64_t n_items = static_cast<int64_t>(p.batch) * p.heads * ((p.d_s + 3) / 4);
+  const int64_t wgs = (n_items + 255) / 256;
+  const int64_t per_xcd = (wgs + 7) / 8;
+  if (8 * per_xcd > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (p.out_bf16)
+    hipLaunchKernelGGL(merge_kernel<true>, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(256), 0,
+                       s, p, n_items, static_cast<int>(per_xcd));
+  else
+    hipLaunchKernelGGL(merge_kernel<false>, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(256), 0,
+                       s, p, n_items, static_cast<int>(per_xcd));
   return hipGetLastError();
 }
 

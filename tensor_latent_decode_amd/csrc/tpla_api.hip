@@ -67,9 +67,10 @@ int64_t generic_smem(int d_s, int d_r) {
   return static_cast<int64_t>(sizeof(float)) * (16LL * (d_s + d_r) + 8LL * (d_s + d_r) + 8LL * d_s + 8 * 16 + 8 * 3);
 }
 
-bool use_mfma(const tpla_decode_args* a) {
+enum class Path { kGeneric, kMfma, kStream };
+
+bool mfma_operands_ok(const tpla_decode_args* a) {
   if (a->dtype != TPLA_BF16) return false;
-  if (!tpla::decode_mfma_supported(a->heads, a->d_s, a->d_r)) return false;
   if (!aligned16(a->q_latent) || !aligned16(a->cache)) return false;
   if ((a->q_latent_stride_b | a->q_latent_stride_h) % 8 != 0) return false;
   if (a->d_r > 0) {
@@ -78,6 +79,15 @@ bool use_mfma(const tpla_decode_args* a) {
   }
   return true;
 }
+
+Path decode_path(const tpla_decode_args* a) {
+  if (!mfma_operands_ok(a)) return Path::kGeneric;
+  if (tpla::decode_stream_supported(a->heads, a->d_s, a->d_r, a->block_size)) return Path::kStream;
+  if (tpla::decode_mfma_supported(a->heads, a->d_s, a->d_r)) return Path::kMfma;
+  return Path::kGeneric;
+}
+
+bool use_mfma(const tpla_decode_args* a) { return decode_path(a) != Path::kGeneric; }
 
 tpla_status check_decode(const tpla_decode_args* a) {
   if (a == nullptr) return fail(TPLA_ERR_NULL, "args is NULL");
@@ -126,9 +136,12 @@ tpla_status plan_decode(const tpla_decode_args* a, Plan* pl) {
     if (st != TPLA_OK) return st;
     int64_t groups = a->batch;
     int per_cu = 2;
-    if (use_mfma(a)) {
+    const Path path = decode_path(a);
+    if (path != Path::kGeneric) {
       groups *= a->heads / (32 * (a->heads % 128 == 0 ? 4 : (a->heads % 64 == 0 ? 2 : 1)));
-      per_cu = tpla::decode_mfma_groups_per_cu(a->heads, a->d_s, a->d_r);
+      per_cu = path == Path::kStream
+                   ? tpla::decode_stream_groups_per_cu(a->heads, a->d_s, a->d_r)
+                   : tpla::decode_mfma_groups_per_cu(a->heads, a->d_s, a->d_r);
     } else {
       groups *= (a->heads + 7) / 8;
     }
@@ -260,10 +273,10 @@ tpla_status tpla_decode_shard(const tpla_decode_args* a, void* workspace, size_t
   p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_o_bytes);
 
   hipError_t e;
-  if (use_mfma(a)) {
-    e = tpla::launch_decode_mfma(p, s);
-  } else {
-    e = tpla::launch_decode_generic(p, a->dtype == TPLA_BF16, s);
+  switch (decode_path(a)) {
+    case Path::kStream: e = tpla::launch_decode_stream(p, s); break;
+    case Path::kMfma: e = tpla::launch_decode_mfma(p, s); break;
+    default: e = tpla::launch_decode_generic(p, a->dtype == TPLA_BF16, s); break;
   }
   if (e != hipSuccess) return hip_status(e, "decode launch");
 
