@@ -17,9 +17,12 @@ namespace {
 
 // One thread per (b, h, 4 consecutive columns); a wavefront covers 256
 // columns of one or more (b, h) rows, so the lse reads are broadcasts and the
-// partial reads are contiguous float4 runs.  Workgroup n handles items
-// ((n % 8) * per_xcd + n / 8) * 256 ..., i.e. sequences are spread over the
-// XCDs in the same order as the split-K kernel placed them.
+// partial reads are contiguous float4 runs.  The split loop is unrolled by 8
+// with all loads issued before they are used; splits without tokens get
+// weight 0 by a select (their workspace rows are read but never trusted).
+// Workgroup n handles items ((n % 8) * per_xcd + n / 8) * 256 ..., i.e.
+// sequences are spread over the XCDs in the same order as the split-K
+// kernel placed them.
 template <bool kBf16Out>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_items, int per_xcd) {
   const int n = blockIdx.x;
@@ -32,8 +35,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_ite
   const int ncol = min(4, p.d_s - col);
   const bool vec = (p.d_s & 3) == 0;
   const int64_t stride_s = static_cast<int64_t>(p.batch) * p.heads;
+  const float* lse_in = p.ws_lse + bh;
   float mx = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.ws_lse[s * stride_s + bh]);
+  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, lse_in[s * stride_s]);
   const int b = static_cast<int>(bh / p.heads);
   const int h = static_cast<int>(bh % p.heads);
   const int64_t obase = b * p.out_sb + h * p.out_sh + col;
@@ -41,20 +45,32 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_ite
   float lse = -INFINITY;
   if (mx != -INFINITY) {
     float tot = 0.f;
-    for (int s = 0; s < p.splits; ++s) {
-      const float l = p.ws_lse[s * stride_s + bh];
-      if (l == -INFINITY) continue;
-      const float w = __expf(l - mx);
-      tot += w;
-      const float* src = p.ws_o + (s * stride_s + bh) * p.d_s + col;
-      if (vec) {
-        const float4 o = *reinterpret_cast<const float4*>(src);
-        acc[0] += w * o.x;
-        acc[1] += w * o.y;
-        acc[2] += w * o.z;
-        acc[3] += w * o.w;
-      } else {
-        for (int i = 0; i < ncol; ++i) acc[i] += w * src[i];
+    const float* o_in = p.ws_o + bh * p.d_s + col;
+    const int64_t o_stride = stride_s * p.d_s;
+    for (int s0 = 0; s0 < p.splits; s0 += 8) {
+      float w[8];
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int s = min(s0 + u, p.splits - 1);
+        const float l = lse_in[s * stride_s];
+        w[u] = (s0 + u < p.splits && l != -INFINITY) ? __expf(l - mx) : 0.f;
+        const float* src = o_in + s * o_stride;
+        if (vec) {
+          v[u] = *reinterpret_cast<const float4*>(src);
+        } else {
+          v[u] = make_float4(src[0], ncol > 1 ? src[1] : 0.f, ncol > 2 ? src[2] : 0.f,
+                             ncol > 3 ? src[3] : 0.f);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool use = w[u] != 0.f;
+        tot += w[u];
+        acc[0] += use ? w[u] * v[u].x : 0.f;
+        acc[1] += use ? w[u] * v[u].y : 0.f;
+        acc[2] += use ? w[u] * v[u].z : 0.f;
+        acc[3] += use ? w[u] * v[u].w : 0.f;
       }
     }
     const float inv = 1.0f / tot;
@@ -62,11 +78,17 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_ite
     for (int i = 0; i < 4; ++i) acc[i] *= inv;
     lse = mx + __logf(tot);
   }
+  const bool out_vec = vec && ((reinterpret_cast<uintptr_t>(static_cast<float*>(p.out) + obase) & 15) == 0);
+  if (out_vec && !kBf16Out) {
+    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + obase) =
+        make_float4(acc[0], acc[1], acc[2], acc[3]);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (i >= ncol) break;
-    if (kBf16Out) static_cast<uint16_t*>(p.out)[obase + i] = f32_to_bf16(acc[i]);
-    else static_cast<float*>(p.out)[obase + i] = acc[i];
+    for (int i = 0; i < 4; ++i) {
+      if (i >= ncol) break;
+      if (kBf16Out) static_cast<uint16_t*>(p.out)[obase + i] = f32_to_bf16(acc[i]);
+      else static_cast<float*>(p.out)[obase + i] = acc[i];
+    }
   }
   if (p.lse != nullptr && col == 0) p.lse[bh] = lse;
 }
