@@ -150,7 +150,10 @@ typedef struct tpla_decode_args {
   int64_t out_stride_b;
   int64_t out_stride_h;
   float* lse;                  /* device float32 [batch, heads] or NULL         */
-  int32_t num_splits;          /* token splits per sequence; 0 = automatic      */
+  int32_t num_splits;          /* token splits per sequence; 0 = automatic.     */
+                               /* A request: raised where a kernel caps the     */
+                               /* tokens of one split (65536 on the bf16        */
+                               /* streaming kernel for 128-head groups)         */
 } tpla_decode_args;
 
 /*

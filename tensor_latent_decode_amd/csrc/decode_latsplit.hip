@@ -1,0 +1,549 @@
+// Streaming bf16 matrix-core split-K decode of one TPLA shard, with the
+// value product split over the latent columns (gfx950).
+//
+// Same computation as decode_stream.hip (per-shard attention of the absorbed
+// query slice plus the whole rope query over the shard's cached rows, value
+// = the latent slice, the shard's own softmax; TPLA abstract, edgentiq blog
+// "How TPLA Works"), with the work of a workgroup divided differently:
+//
+//   scores   wave w owns heads 32w .. 32w+31 of the group:
+//            S^T[token, head] = K_tile . Q^T, then P = exp2(c*S - m_ref)
+//   values   wave w owns latent columns 32*MPW*w .. +32*MPW, for every head
+//            of the group: O^T[lat, head] += V^T . P^T
+//
+// The matrix cores wait on operand loads (about 30 cycles per KiB a wave
+// moves from LDS into registers while MFMAs run), so the point of the split
+// is to move fewer bytes per MFMA:
+// * P^T fragments are exchanged through LDS (each wave writes its 32 heads,
+//   4 KiB per tile) and each fragment feeds MPW value MFMAs.
+// * V^T never goes through LDS.  The value A operand needs 8 consecutive
+//   tokens of one latent column per lane; the score A operand (K rows) is
+//   already in registers, and an MFMA with a 0/1 B operand moves it into
+//   the accumulator layout, which is exactly that fragment layout:
+//       D = K(ks=2m) . I_lo + K(ks=2m+1) . I_hi
+//   gives rows = tokens, columns = latent 32m .. 32m+31 (each output is one
+//   bf16 value times 1 plus exact zeros, so the round trip through fp32 and
+//   back to bf16 is exact for finite values).  Each wave transposes only its
+//   own MPW latent tiles; it visits their k-steps first (the k-step order is
+//   rotated per wave, and the query fragments are loaded in that order).
+// * Tiles go from HBM straight into LDS (global_load_lds_dwordx4 from
+//   inline assembly, waited for explicitly) in the swizzled layout of the
+//   other streaming kernel, conflict-free for the score A-fragment reads.
+//   Three K buffers: tile i+3 is copied while tiles i+1 and i+2 are in
+//   use, so a copy has a whole step to land.  The copy instructions are
+//   spread over the score MFMAs: issued back to back they hold the wave
+//   for about as long as the vector memory unit takes to accept them.
+// * The P^T fragments are stored as soon as each is complete, and the
+//   cross-half max uses v_permlane32_swap, so no LDS wait ends a step.
+// * Softmax against a fixed reference max (the split's first tile max); a
+//   later tile max more than 64 (base 2) above it makes the split run again
+//   with the raised reference.  Accumulators are touched only by MFMAs.
+// * Work units are spread so that the splits of a sequence share an XCD.
+#include <type_traits>
+
+#include "tpla_internal.h"
+
+namespace tpla {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+
+// Scalar (constant address space) read of a wave-uniform int32.
+__device__ __forceinline__ int scalar_load(const int32_t* p) { return *(const const_i32_t*)p; }
+
+constexpr int kTile = 64;
+constexpr int kMaxTiles = 1024;     // tiles per split (the host plans splits to fit)
+constexpr float kRescale = 64.0f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+// XOR pattern of tile row r: bit2 = r1, bit1 = r0 ^ r3, bit0 = r2.
+__device__ __forceinline__ int swz(int r) {
+  return (((r >> 1) & 1) << 2) | (((r ^ (r >> 3)) & 1) << 1) | ((r >> 2) & 1);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
+}
+
+// One 16-byte global -> LDS copy per lane, to LDS address lds + 16*lane.
+__device__ __forceinline__ void copy16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory");
+}
+
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));   // vmcnt(0) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ f32x16_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int NW, int DS, int DR>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(1, 1)))
+void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
+  constexpr int D = DS + DR;
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int SLOTS = kTile * CPR;        // chunks per tile
+  constexpr int NT = NW * 64;
+  constexpr int IPT = SLOTS / NT;           // copies per thread per tile
+  constexpr int KS = D / 16;                // k-steps of the score product
+  constexpr int KL = DS / 16;               // ... of which latent
+  constexpr int MT = DS / 32;               // 32-column latent tiles
+  constexpr int MPW = MT / NW;              // latent tiles per wave (value product)
+  constexpr int NPF = NW * 4;               // P^T fragments per tile: (head tile, k-step)
+  constexpr int NPV = NPF * MPW;            // value MFMAs per wave per tile
+  constexpr int VPS = 32 / NPV;             // scores exponentiated per value MFMA
+  static_assert(SLOTS % NT == 0, "tile must split evenly over the workgroup");
+  static_assert(CPR % 8 == 0 && DS % 64 == 0 && DR % 16 == 0, "shape");
+  static_assert(MT % NW == 0 && MPW % 2 == 0, "latent tiles per wave");
+  static_assert(((KL / 4) & (KL / 4 - 1)) == 0, "latent k-step groups must be a power of two");
+  static_assert(32 % NPV == 0 && KS > 2 * MPW, "schedule shape");
+  static_assert(2 * IPT <= KS && IPT < 64, "copies per tile must fit the score k-steps");
+
+  constexpr int NB = 3;                     // K buffers
+  __shared__ __attribute__((aligned(1024))) uint4 ktile[NB][SLOTS];
+  __shared__ __attribute__((aligned(1024))) uint4 ptile[2][NPF * 64];
+  __shared__ uint32_t trow[kMaxTiles];   // first cache row of each tile / 64
+
+  // ---- work unit (XCD-aware) ----
+  const int n = blockIdx.x;
+  const int u = (n & 7) * units_per_xcd + (n >> 3);
+  if (u >= n_units) return;
+  const int S = p.num_splits;
+  const int HG = p.heads / (32 * NW);
+  const int split = u % S;
+  const int bh = u / S;
+  const int hg = bh % HG;
+  const int b = bh / HG;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int l31 = lane & 31, half = lane >> 5;
+  const int head0 = hg * (32 * NW);              // first head of the group
+  const int head = head0 + wave * 32 + l31;      // this lane's score head
+
+  int L = scalar_load(p.seq_lens + b);
+  L = max(0, min(L, min(p.max_seq_len, p.max_blocks * p.block_size)));
+  const int t0 = split * p.chunk;
+  const int t1 = min(L, t0 + p.chunk);
+  const int64_t row0 = (static_cast<int64_t>(split) * p.batch + b) * p.heads;
+  if (t0 >= t1) {
+    if (half == 0) p.ws_lse[row0 + head] = -INFINITY;
+    return;
+  }
+  const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+  const int nfull = (t1 - t0) / kTile;
+
+  // ---- k-step order: latent k-steps rotated so this wave's own latent
+  // tiles (k-steps 2*MPW*wave ..) come first, then the rope k-steps ----
+  const int rot4 = (MPW / 2) * wave;             // rotation in groups of 4 k-steps
+  auto phys_ks = [&](int kk) -> int {
+    return kk < KL ? (((kk >> 2) + rot4) & (KL / 4 - 1)) * 4 + (kk & 3) : kk;
+  };
+
+  bf16x8_t qf[KS];       // query fragments, loaded once the first copies are out
+  bf16x8_t ident[2];     // 0/1 B operands of the transposing MFMAs
+
+  // ---- tile copies: chunk slot (i*NW + wave)*64 + lane of a tile ----
+  uint32_t src_off[IPT];
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int slot = (i * NW + wave) * 64 + lane;
+    const int r = slot / CPR;
+    const int pc = slot % CPR;
+    const int c = (pc & ~7) | ((pc & 7) ^ swz(r));
+    src_off[i] = static_cast<uint32_t>((r * D + c * 8) * 2);
+  }
+  const uint16_t* cache = static_cast<const uint16_t*>(p.cache);
+  const int32_t* bt_row = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
+  const int bs = p.block_size;
+  // First cache row of tile t, in units of 64 rows; an out-of-range block
+  // id reads the cache's first rows (unspecified output, no access outside
+  // the cache).
+  auto tile_row = [&](int t, int page) -> uint32_t {
+    const int tb = t0 + t * kTile;
+    const bool ok = page >= 0 && page < p.num_blocks;
+    return ok ? static_cast<uint32_t>(page) * static_cast<uint32_t>(bs / kTile) +
+                    static_cast<uint32_t>((tb % bs) / kTile)
+              : 0u;
+  };
+
+  // Copy of tile t into K buffer kb, issued one 16-byte chunk per lane at a
+  // time.  Rows past the split end copy the same chunk of the tile's row 0
+  // (finite; their scores are masked).  A tile past the split's last one
+  // becomes a harmless re-read of the cache's first row (every copy slot
+  // issues the same number of instructions, so the wait counts are fixed).
+  struct CopyJob {
+    const uint16_t* base;
+    uint32_t lim;      // bytes of valid rows
+    uint32_t lds;
+  };
+  auto make_job = [&](int t, int kb, uint32_t row64) -> CopyJob {
+    CopyJob j;
+    j.lds = lds_addr(&ktile[kb][0]);
+    if (t < ntiles) {
+      const int nvalid = min(kTile, t1 - (t0 + t * kTile));
+      j.base = cache + static_cast<int64_t>(row64) * (kTile * D);
+      j.lim = static_cast<uint32_t>(nvalid * 2 * D);
+    } else {
+      j.base = cache;
+      j.lim = 0;
+    }
+    return j;
+  };
+  auto copy_chunk = [&](const CopyJob& j, int ci) {
+    const uint32_t off = src_off[ci] < j.lim ? src_off[ci] : src_off[ci] % (2 * D);
+    copy16(j.base, off, j.lds + static_cast<uint32_t>((ci * NW + wave) * 64 * 16));
+  };
+  auto copy_all = [&](const CopyJob& j) {
+#pragma unroll
+    for (int ci = 0; ci < IPT; ++ci) copy_chunk(j, ci);
+  };
+  // Wait until at most n tile copies of this wave are in flight.
+  auto wait_vm = [&](auto n) {
+    constexpr int N = decltype(n)::value;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+  };
+
+  // Score A fragment (rows 32*mt + l31, k-step phys_ks(kk)) of the tile at T.
+  int qk_off[4];
+  {
+    const int g = half ^ swz(l31);
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) qk_off[k2] = (l31 * CPR + ((2 * k2) ^ g)) * 16;
+  }
+  auto rd_k = [&](const char* T, int kk, int mt) -> bf16x8_t {
+    const int grp = phys_ks(kk) >> 2;   // wave-uniform
+    return *reinterpret_cast<const bf16x8_t*>(T + qk_off[kk & 3] + mt * 32 * CPR * 16 + grp * 128);
+  };
+
+  f32x16_t oacc[MPW][NW];    // O^T tiles: latent tile MPW*wave + mm, head tile ht
+  bf16x8_t vc[MPW][4];       // V^T fragments of the tile whose values are due
+  float m_run = -INFINITY;   // reference max of the scaled (base-2) scores
+  float l_part = 0.f;        // this lane's share of its head's row sum
+  float m_seen;              // largest tile max that overflowed
+  const float c = p.scale_log2;
+
+  // Scores of the tile at T and the V^T fragments of this wave's latent
+  // tiles; k-steps in rotated order with the A reads two k-steps ahead.
+  auto scores = [&](const char* T, f32x16_t (&sc)[2], bf16x8_t (&vt)[MPW][4], const CopyJob* cj) {
+#pragma unroll
+    for (int m = 0; m < MPW; ++m)
+#pragma unroll
+      for (int ht = 0; ht < NW; ++ht) asm volatile("" : "+a"(oacc[m][ht]));
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[mt][r] = 0.f;
+    f32x16_t tacc[2];
+    bf16x8_t qa[4];
+    qa[0] = rd_k(T, 0, 0);
+    qa[1] = rd_k(T, 0, 1);
+    qa[2] = rd_k(T, 1, 0);
+    qa[3] = rd_k(T, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      sc[0] = mfma(qa[(2 * kk) & 3], qf[kk], sc[0]);
+      if (kk >= 2 && kk <= 2 * MPW && (kk & 1) == 0) {
+        // latent tile (kk - 2) / 2 is transposed: A fragments of the value
+        // product for token k-steps j = 2*mt + hf
+        const int mm = (kk - 2) >> 1;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vt[mm][2 * mt + hf][e] = static_cast<__bf16>(tacc[mt][8 * hf + e]);
+      }
+      if (kk < 2 * MPW) {
+        const f32x16_t z = {};
+        tacc[0] = mfma(qa[(2 * kk) & 3], ident[kk & 1], (kk & 1) ? tacc[0] : z);
+      }
+      if (kk + 2 < KS) qa[(2 * kk) & 3] = rd_k(T, kk + 2, 0);
+      sc[1] = mfma(qa[(2 * kk + 1) & 3], qf[kk], sc[1]);
+      if (kk < 2 * MPW) {
+        const f32x16_t z = {};
+        tacc[1] = mfma(qa[(2 * kk + 1) & 3], ident[kk & 1], (kk & 1) ? tacc[1] : z);
+      }
+      if (kk + 2 < KS) qa[(2 * kk + 1) & 3] = rd_k(T, kk + 2, 1);
+      if ((kk & 1) == 0 && kk / 2 < IPT && cj != nullptr) copy_chunk(*cj, kk / 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // The other lane of this lane's head (lane l +- 32): one of the two swap
+  // results is the lane's own value, the other its partner's.
+  auto both_halves_max = [](float v) -> float {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+  auto both_halves_sum = [](float v) -> float {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  };
+
+  // Scaled max of this lane's head over the tile (both lanes of the head).
+  auto tile_max = [&](const f32x16_t (&sc)[2]) -> float {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mt][r]);
+    return both_halves_max(mx) * c;
+  };
+
+  // Score v of this lane (0..31): token row of the tile and its P^T slot.
+  //   sc[v >> 4][v & 15] is row (v >> 4)*32 + 8*((v & 15) >> 2) + 4*half + (v & 3),
+  //   and P^T fragment j = v >> 3, element v & 7.
+  auto put_p = [&](uint4* dst, const bf16x8_t (&pn)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[(wave * 4 + j) * 64 + lane] = __builtin_bit_cast(uint4, pn[j]);
+  };
+
+  // Value product of the tile whose P^T is in ptile[pb] and V^T in vc,
+  // with the exponentials of the next tile's scores sc interleaved (masked
+  // rows >= lim get P = 0); the new P^T goes to pn.
+  auto values = [&](int pb, const f32x16_t (&sc)[2], int lim, bool masked, uint4* pdst,
+                    float& mx) {
+    const uint4* P = &ptile[pb][0];
+    bf16x8_t pn[4];
+    auto frag = [&](int f) -> bf16x8_t {
+      const int ht = f % NW, j = f / NW;
+      return __builtin_bit_cast(bf16x8_t, P[(ht * 4 + j) * 64 + lane]);
+    };
+    bf16x8_t pa[3];
+    pa[0] = frag(0);
+    pa[1] = frag(1);
+    pa[2] = frag(2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < NPF; ++f) {
+      const int ht = f % NW, j = f / NW;
+#pragma unroll
+      for (int mm = 0; mm < MPW; ++mm) {
+        oacc[mm][ht] = mfma(vc[mm][j], pa[f % 3], oacc[mm][ht]);
+#pragma unroll
+        for (int e = 0; e < VPS; ++e) {
+          const int v = (f * MPW + mm) * VPS + e;
+          float sv = sc[v >> 4][v & 15];
+          if (masked) {
+            const int row = (v >> 4) * 32 + 8 * ((v & 15) >> 2) + (v & 3);
+            sv = (row >= lim) ? -INFINITY : sv;
+          }
+          mx = fmaxf(mx, sv);
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -m_run));
+          l_part += pv;
+          pn[v >> 3][v & 7] = static_cast<__bf16>(pv);
+          if ((v & 7) == 7) pdst[(wave * 4 + (v >> 3)) * 64 + lane] = __builtin_bit_cast(uint4, pn[v >> 3]);
+        }
+      }
+      if (f + 3 < NPF) pa[f % 3] = frag(f + 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Value product only (after the last tile).
+  auto values_last = [&](int pb) {
+    const uint4* P = &ptile[pb][0];
+#pragma unroll
+    for (int f = 0; f < NPF; ++f) {
+      const int ht = f % NW, j = f / NW;
+      const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, P[(ht * 4 + j) * 64 + lane]);
+#pragma unroll
+      for (int mm = 0; mm < MPW; ++mm) oacc[mm][ht] = mfma(vc[mm][j], pa, oacc[mm][ht]);
+    }
+  };
+
+  // Pipeline (tile t in K buffer t % 3, its P^T in ptile[t % 2]):
+  //   step i:  barrier (tile i+1 copied, P^T of tile i written by every
+  //            wave; every wave is done with tile i's K buffer and with
+  //            ptile[(i+1) % 2])
+  //            scores of tile i+1 and its V^T (this wave's latent tiles),
+  //            with the copy of tile i+3 -> K buffer i % 3 spread over it
+  //            values of tile i, interleaved with P of tile i+1, whose
+  //            fragments go to ptile[(i+1) % 2] as they complete
+  //            wait for this wave's copies of tile i+2
+  auto step = [&](int i, bool masked) {
+    // The tile table read waits for this wave's LDS traffic, as the
+    // barrier does anyway.
+    const uint32_t row64 = __builtin_amdgcn_readfirstlane(trow[min(i + 3, ntiles - 1)]);
+    const CopyJob cj = make_job(i + 3, i % NB, row64);
+    barrier();
+    const char* T = reinterpret_cast<const char*>(&ktile[(i + 1) % NB][0]);
+    f32x16_t sc[2];
+    bf16x8_t vn[MPW][4];
+    scores(T, sc, vn, &cj);
+    const int lim = t1 - (t0 + (i + 1) * kTile) - 4 * half;
+    float mx = -INFINITY;
+    values(i & 1, sc, lim, masked, &ptile[(i + 1) & 1][0], mx);
+#pragma unroll
+    for (int m = 0; m < MPW; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vc[m][j] = vn[m][j];
+    mx = both_halves_max(mx) * c;
+    if (mx > m_run + kRescale) m_seen = fmaxf(m_seen, mx);
+    wait_vm(std::integral_constant<int, IPT>());
+  };
+
+  // ---- prologue: first three tiles in flight before anything else ----
+  // (block ids of tiles 0..2 straight from the block table; the table of
+  // all tiles goes to LDS for the steps)
+  {
+    int pg[3];
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      pg[t] = t < ntiles ? scalar_load(bt_row + (t0 + t * kTile) / bs) : 0;
+#pragma unroll
+    for (int t = 0; t < 3; ++t) copy_all(make_job(t, t, tile_row(t, pg[t])));
+  }
+  // ---- query fragments (B operand of S^T) in rotated order ----
+  {
+    const uint16_t* ql = static_cast<const uint16_t*>(p.q_latent) + b * p.qls_b + head * p.qls_h;
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + b * p.qrs_b + head * p.qrs_h;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int k = phys_ks(kk) * 16 + 8 * half;
+      qf[kk] = *reinterpret_cast<const bf16x8_t*>((k < DS) ? (ql + k) : (qr + (k - DS)));
+    }
+  }
+  // 0/1 B operands: ident[0] picks k = j, ident[1] picks k = j - 16 for
+  // output column j (lane l holds column l % 32, k-slots 8*(l/32) ..).
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ident[0][e] = static_cast<__bf16>((l31 == 8 * half + e) ? 1.0f : 0.0f);
+    ident[1][e] = static_cast<__bf16>((l31 == 16 + 8 * half + e) ? 1.0f : 0.0f);
+  }
+
+  for (int t = threadIdx.x; t < min(ntiles, kMaxTiles); t += NT)
+    trow[t] = tile_row(t, bt_row[(t0 + t * kTile) / bs]);
+
+  bool first = true;
+  while (true) {
+#pragma unroll
+    for (int m = 0; m < MPW; ++m)
+#pragma unroll
+      for (int ht = 0; ht < NW; ++ht)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[m][ht][r] = 0.f;
+    l_part = 0.f;
+    m_seen = -INFINITY;
+    if (!first) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t) copy_all(make_job(t, t, __builtin_amdgcn_readfirstlane(trow[min(t, ntiles - 1)])));
+    }
+    wait_vm(std::integral_constant<int, IPT>());
+    barrier();
+    {
+      f32x16_t sc[2];
+      scores(reinterpret_cast<const char*>(&ktile[0][0]), sc, vc, nullptr);
+      if (nfull == 0) {
+        const int lim = t1 - t0 - 4 * half;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (mt * 32 + 8 * (r >> 2) + (r & 3) >= lim) sc[mt][r] = -INFINITY;
+      }
+      const float mx0 = tile_max(sc);
+      m_run = first ? mx0 : fmaxf(m_run, mx0);
+      first = false;
+      bf16x8_t pn[4];
+#pragma unroll
+      for (int v = 0; v < 32; ++v) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v >> 4][v & 15], c, -m_run));
+        l_part += pv;
+        pn[v >> 3][v & 7] = static_cast<__bf16>(pv);
+      }
+      put_p(&ptile[0][0], pn);
+    }
+    for (int i = 0; i + 1 < nfull; ++i) step(i, false);
+    if (nfull >= 1 && nfull < ntiles) step(nfull - 1, true);
+    wait_copies();   // the trailing re-reads land before any K buffer is reused
+    barrier();
+    values_last((ntiles - 1) & 1);
+    // compare notes: one flag per wave in K buffer 0 (idle after the barrier)
+    int* flags = reinterpret_cast<int*>(&ktile[0][0]);
+    const bool over = __ballot(m_seen != -INFINITY) != 0ull;
+    if (lane == 0) flags[wave] = over ? 1 : 0;
+    barrier();
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any |= flags[w];
+    if (!any) break;
+    m_run = fmaxf(m_run, m_seen);
+    barrier();   // every wave has read the flags before the buffers are refilled
+  }
+
+  // ---- split result: o = U / l, lse = m + log l (natural log) ----
+  // Row sums go through K buffer 1 (idle): the value tiles of a head live
+  // in every wave, its sum in the wave that scored it.
+  const float l_tot = both_halves_sum(l_part);
+  float* lsum = reinterpret_cast<float*>(&ktile[1][0]);
+  if (half == 0) {
+    lsum[wave * 32 + l31] = l_tot;
+    p.ws_lse[row0 + head] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+  barrier();
+#pragma unroll
+  for (int ht = 0; ht < NW; ++ht) {
+    const float inv = 1.0f / lsum[ht * 32 + l31];
+    float* wo = p.ws_o + (row0 + head0 + ht * 32 + l31) * DS + 32 * MPW * wave + 4 * half;
+#pragma unroll
+    for (int mm = 0; mm < MPW; ++mm)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4_t v;
+        v[0] = oacc[mm][ht][4 * q + 0] * inv;
+        v[1] = oacc[mm][ht][4 * q + 1] * inv;
+        v[2] = oacc[mm][ht][4 * q + 2] * inv;
+        v[3] = oacc[mm][ht][4 * q + 3] * inv;
+        *reinterpret_cast<f32x4_t*>(wo + mm * 32 + 8 * q) = v;
+      }
+  }
+}
+
+template <int NW, int DS, int DR>
+hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
+  if (p.chunk > kMaxTiles * kTile) return hipErrorInvalidValue;
+  const int HG = p.heads / (32 * NW);
+  const int n_units = p.num_splits * p.batch * HG;
+  const int per_xcd = (n_units + 7) / 8;
+  hipLaunchKernelGGL((decode_latsplit_kernel<NW, DS, DR>), dim3(8 * per_xcd), dim3(NW * 64), 0, s,
+                     p, n_units, per_xcd);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_latsplit_max_chunk() { return kMaxTiles * kTile; }
+
+bool decode_latsplit_supported(int heads, int d_s, int d_r, int block_size) {
+  return block_size % kTile == 0 && heads % 128 == 0 && d_s == 256 && d_r == 64;
+}
+
+hipError_t launch_decode_latsplit(const DecodeParams& p, hipStream_t s) {
+  if (decode_latsplit_supported(p.heads, p.d_s, p.d_r, p.block_size)) return launch_t<4, 256, 64>(p, s);
+  return hipErrorNotSupported;
+}
+
+}  // namespace tpla

@@ -503,6 +503,7 @@ int decode_stream_groups_per_cu(int heads, int d_s, int d_r) {
 }
 
 hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t s) {
+  if (decode_latsplit_supported(p.heads, p.d_s, p.d_r, p.block_size)) return launch_decode_latsplit(p, s);
   if (p.heads % 128 == 0 && p.d_s == 256 && p.d_r == 64) return launch_t<4, 256, 64, 1>(p, s);
   if (p.heads % 64 == 0 && p.d_s == 128 && p.d_r == 64) return launch_t<2, 128, 64, 2>(p, s);
   return hipErrorNotSupported;

@@ -150,6 +150,12 @@ tpla_status plan_decode(const tpla_decode_args* a, Plan* pl) {
   }
   const int max_tiles = std::max(1, (maxlen + 63) / 64);
   want = std::min(want, max_tiles);
+  if (decode_path(a) == Path::kStream &&
+      tpla::decode_latsplit_supported(a->heads, a->d_s, a->d_r, a->block_size)) {
+    // a split must fit the kernel's LDS table of tiles
+    const int cap = tpla::decode_latsplit_max_chunk();
+    want = std::max(want, static_cast<int>((static_cast<int64_t>(maxlen) + cap - 1) / cap));
+  }
   const int tiles_per = (max_tiles + want - 1) / want;
   pl->chunk = tiles_per * 64;
   pl->splits = std::max(1, (maxlen + pl->chunk - 1) / pl->chunk);

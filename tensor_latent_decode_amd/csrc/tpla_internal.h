@@ -85,6 +85,9 @@ int decode_mfma_groups_per_cu(int heads, int d_s, int d_r);
 hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t s);
 bool decode_stream_supported(int heads, int d_s, int d_r, int block_size);
 int decode_stream_groups_per_cu(int heads, int d_s, int d_r);
+hipError_t launch_decode_latsplit(const DecodeParams& p, hipStream_t s);
+bool decode_latsplit_supported(int heads, int d_s, int d_r, int block_size);
+int decode_latsplit_max_chunk();   // tokens per split the latent-split kernel accepts
 hipError_t launch_decode_generic(const DecodeParams& p, int is_bf16, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_combine(const PartPtrs& parts, int part_bf16, int tp, int batch, int heads,
