@@ -65,7 +65,8 @@ def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tensor_latent_decode_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.startswith("decode_") or name == "tpla_api.hip":
+        if name.startswith("decode_") or name in ("tpla_api.hip", "merge_combine.hip",
+                                                  "tpla_internal.h"):
             h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 

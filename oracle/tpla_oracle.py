@@ -23,7 +23,7 @@ Attention for Efficient Disaggregated Prefill & Decode Inference"):
   local computations approximate the global score).
 
 The pages print no equations.  Where they leave a step open the plain reading
-is taken (listed in DESIGN.md, "Readings"):
+is taken:
 
 * The rope key/query are not part of the latent: every shard carries them
   whole and adds their score term (reading R1).

@@ -405,26 +405,28 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     wait_vm(std::integral_constant<int, IPT>());
   };
 
-  // ---- prologue: first three tiles in flight before anything else ----
-  // (block ids of tiles 0..2 straight from the block table; the table of
-  // all tiles goes to LDS for the steps)
+  // ---- prologue ----
+  // Tiles 0 and 1 go out first, then the query loads; the compiler's wait
+  // for the query (it cannot see the copies) then also covers tiles 0 and
+  // 1, which the first score product needs anyway.  Tile 2 is issued after
+  // that wait so that it does not hold the first step back.
   {
     int pg[3];
 #pragma unroll
     for (int t = 0; t < 3; ++t)
       pg[t] = t < ntiles ? scalar_load(bt_row + (t0 + t * kTile) / bs) : 0;
-#pragma unroll
-    for (int t = 0; t < 3; ++t) copy_all(make_job(t, t, tile_row(t, pg[t])));
-  }
-  // ---- query fragments (B operand of S^T) in rotated order ----
-  {
+    copy_all(make_job(0, 0, tile_row(0, pg[0])));
+    copy_all(make_job(1, 1, tile_row(1, pg[1])));
     const uint16_t* ql = static_cast<const uint16_t*>(p.q_latent) + b * p.qls_b + head * p.qls_h;
     const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + b * p.qrs_b + head * p.qrs_h;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const int k = phys_ks(kk) * 16 + 8 * half;
+      const int k = phys_ks(kk) * 16 + 8 * half;   // query fragments in rotated order
       qf[kk] = *reinterpret_cast<const bf16x8_t*>((k < DS) ? (ql + k) : (qr + (k - DS)));
     }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) asm volatile("" : : "v"(qf[kk]));
+    copy_all(make_job(2, 2, tile_row(2, pg[2])));
   }
   // 0/1 B operands: ident[0] picks k = j, ident[1] picks k = j - 16 for
   // output column j (lane l holds column l % 32, k-slots 8*(l/32) ..).
@@ -433,9 +435,12 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     ident[0][e] = static_cast<__bf16>((l31 == 8 * half + e) ? 1.0f : 0.0f);
     ident[1][e] = static_cast<__bf16>((l31 == 16 + 8 * half + e) ? 1.0f : 0.0f);
   }
-
-  for (int t = threadIdx.x; t < min(ntiles, kMaxTiles); t += NT)
-    trow[t] = tile_row(t, bt_row[(t0 + t * kTile) / bs]);
+  // Table of tile rows for the steps (scalar reads: a vector load's wait
+  // would also wait for tile 2).
+  for (int t = wave; t < min(ntiles, kMaxTiles); t += NW) {
+    const uint32_t r = tile_row(t, scalar_load(bt_row + (t0 + t * kTile) / bs));
+    if (lane == 0) trow[t] = r;
+  }
 
   bool first = true;
   while (true) {
@@ -450,8 +455,8 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     if (!first) {
 #pragma unroll
       for (int t = 0; t < 3; ++t) copy_all(make_job(t, t, __builtin_amdgcn_readfirstlane(trow[min(t, ntiles - 1)])));
+      wait_vm(std::integral_constant<int, IPT>());
     }
-    wait_vm(std::integral_constant<int, IPT>());
     barrier();
     {
       f32x16_t sc[2];
@@ -504,21 +509,40 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     p.ws_lse[row0 + head] = (m_run + __log2f(l_tot)) * kLn2;
   }
   barrier();
+  // Split outputs leave as fp16 with one float scale per (row, wave block
+  // of 32*MPW columns): o = scale * h, |h| <= 1.  That halves the partial
+  // traffic of the split merge at a rounding error below 2^-11 of the
+  // block's largest value.
+  uint16_t* wh = reinterpret_cast<uint16_t*>(p.ws_o);
+  float* wsc = reinterpret_cast<float*>(reinterpret_cast<char*>(p.ws_o) +
+                                        fp16_partials_scale_offset(p.num_splits, p.batch, p.heads, DS));
 #pragma unroll
   for (int ht = 0; ht < NW; ++ht) {
-    const float inv = 1.0f / lsum[ht * 32 + l31];
-    float* wo = p.ws_o + (row0 + head0 + ht * 32 + l31) * DS + 32 * MPW * wave + 4 * half;
+    const float inv_l = 1.0f / lsum[ht * 32 + l31];
+    float amax = 0.f;
+#pragma unroll
+    for (int mm = 0; mm < MPW; ++mm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(oacc[mm][ht][r]));
+    amax = both_halves_max(amax);
+    const float hs = amax > 0.f ? 1.0f / amax : 0.f;
+    const int64_t row = row0 + head0 + ht * 32 + l31;
+    uint16_t* dst = wh + row * DS + 32 * MPW * wave + 4 * half;
 #pragma unroll
     for (int mm = 0; mm < MPW; ++mm)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        f32x4_t v;
-        v[0] = oacc[mm][ht][4 * q + 0] * inv;
-        v[1] = oacc[mm][ht][4 * q + 1] * inv;
-        v[2] = oacc[mm][ht][4 * q + 2] * inv;
-        v[3] = oacc[mm][ht][4 * q + 3] * inv;
-        *reinterpret_cast<f32x4_t*>(wo + mm * 32 + 8 * q) = v;
+        uint32_t w[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const _Float16 lo = static_cast<_Float16>(oacc[mm][ht][4 * q + 2 * k] * hs);
+          const _Float16 hi = static_cast<_Float16>(oacc[mm][ht][4 * q + 2 * k + 1] * hs);
+          w[k] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+        }
+        *reinterpret_cast<uint2*>(dst + mm * 32 + 8 * q) = make_uint2(w[0], w[1]);
       }
+    if (half == 0) wsc[row * NW + wave] = amax * inv_l;
   }
 }
 
@@ -536,6 +560,8 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
 }  // namespace
 
 int decode_latsplit_max_chunk() { return kMaxTiles * kTile; }
+
+int decode_latsplit_partial_block() { return 64; }
 
 bool decode_latsplit_supported(int heads, int d_s, int d_r, int block_size) {
   return block_size % kTile == 0 && heads % 128 == 0 && d_s == 256 && d_r == 64;

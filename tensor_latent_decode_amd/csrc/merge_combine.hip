@@ -4,8 +4,9 @@
 // output over its own tokens o_s (already divided by its own sum) and
 // lse_s = log sum exp(scores).  The split results combine exactly:
 //     LSE = log sum_s exp(lse_s),   o = sum_s exp(lse_s - LSE) * o_s.
-// Splits without tokens carry lse_s = -inf and are skipped (their o_s is
-// never read).
+// Splits without tokens carry lse_s = -inf and get weight 0.  o_s comes as
+// float32, or as fp16 h_s with a float scale per block of columns
+// (o_s = scale * h_s).
 //
 // Combine: shard g owns latent columns g*d_s .. (g+1)*d_s, so summing the
 // zero-padded shard outputs (the all-reduce of the TPLA abstract) places
@@ -23,7 +24,32 @@ namespace {
 // Workgroup n handles items ((n % 8) * per_xcd + n / 8) * 256 ..., i.e.
 // sequences are spread over the XCDs in the same order as the split-K
 // kernel placed them.
-template <bool kBf16Out>
+// Four consecutive columns of split s's output for row bh (float32 or
+// scaled fp16 partials).
+template <bool kFp16Parts>
+__device__ __forceinline__ float4 load_part(const MergeParams& p, int s, int64_t bh, int col, int ncol,
+                                            bool vec, int64_t stride_s) {
+  if constexpr (kFp16Parts) {
+    const int64_t row = s * stride_s + bh;
+    const uint16_t* h = reinterpret_cast<const uint16_t*>(p.ws_o) + row * p.d_s + col;
+    const float* sc = reinterpret_cast<const float*>(
+        reinterpret_cast<const char*>(p.ws_o) +
+        fp16_partials_scale_offset(p.splits, p.batch, p.heads, p.d_s));
+    const float f = sc[row * (p.d_s / p.blk_cols) + col / p.blk_cols];
+    const uint2 w = *reinterpret_cast<const uint2*>(h);
+    return make_float4(f * static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w.x))),
+                       f * static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w.x >> 16))),
+                       f * static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w.y))),
+                       f * static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w.y >> 16))));
+  } else {
+    const float* src = p.ws_o + (s * stride_s + bh) * p.d_s + col;
+    if (vec) return *reinterpret_cast<const float4*>(src);
+    return make_float4(src[0], ncol > 1 ? src[1] : 0.f, ncol > 2 ? src[2] : 0.f,
+                       ncol > 3 ? src[3] : 0.f);
+  }
+}
+
+template <bool kBf16Out, bool kFp16Parts>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_items, int per_xcd) {
   const int n = blockIdx.x;
   const int64_t wg = static_cast<int64_t>(n & 7) * per_xcd + (n >> 3);
@@ -45,8 +71,6 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_ite
   float lse = -INFINITY;
   if (mx != -INFINITY) {
     float tot = 0.f;
-    const float* o_in = p.ws_o + bh * p.d_s + col;
-    const int64_t o_stride = stride_s * p.d_s;
     for (int s0 = 0; s0 < p.splits; s0 += 8) {
       float w[8];
       float4 v[8];
@@ -55,13 +79,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_ite
         const int s = min(s0 + u, p.splits - 1);
         const float l = lse_in[s * stride_s];
         w[u] = (s0 + u < p.splits && l != -INFINITY) ? __expf(l - mx) : 0.f;
-        const float* src = o_in + s * o_stride;
-        if (vec) {
-          v[u] = *reinterpret_cast<const float4*>(src);
-        } else {
-          v[u] = make_float4(src[0], ncol > 1 ? src[1] : 0.f, ncol > 2 ? src[2] : 0.f,
-                             ncol > 3 ? src[3] : 0.f);
-        }
+        v[u] = load_part<kFp16Parts>(p, s, bh, col, ncol, vec, stride_s);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -130,17 +148,26 @@ hipError_t launch_c(const PartPtrs& parts, int tp, int batch, int heads, int d_s
 
 }  // namespace
 
+template <bool kBf16Out, bool kFp16Parts>
+void launch_m(const MergeParams& p, int64_t n_items, int64_t per_xcd, hipStream_t s) {
+  hipLaunchKernelGGL((merge_kernel<kBf16Out, kFp16Parts>), dim3(static_cast<unsigned>(8 * per_xcd)),
+                     dim3(256), 0, s, p, n_items, static_cast<int>(per_xcd));
+}
+
 hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
   const int64_t n_items = static_cast<int64_t>(p.batch) * p.heads * ((p.d_s + 3) / 4);
   const int64_t wgs = (n_items + 255) / 256;
   const int64_t per_xcd = (wgs + 7) / 8;
   if (8 * per_xcd > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (p.out_bf16)
-    hipLaunchKernelGGL(merge_kernel<true>, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(256), 0,
-                       s, p, n_items, static_cast<int>(per_xcd));
-  else
-    hipLaunchKernelGGL(merge_kernel<false>, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(256), 0,
-                       s, p, n_items, static_cast<int>(per_xcd));
+  // fp16 partials: 4-column groups never straddle a scale block
+  if (p.blk_cols != 0 && (p.blk_cols % 4 != 0 || p.d_s % p.blk_cols != 0)) return hipErrorInvalidValue;
+  if (p.blk_cols != 0) {
+    if (p.out_bf16) launch_m<true, true>(p, n_items, per_xcd, s);
+    else launch_m<false, true>(p, n_items, per_xcd, s);
+  } else {
+    if (p.out_bf16) launch_m<true, false>(p, n_items, per_xcd, s);
+    else launch_m<false, false>(p, n_items, per_xcd, s);
+  }
   return hipGetLastError();
 }
 

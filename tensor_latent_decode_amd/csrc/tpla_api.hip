@@ -293,6 +293,10 @@ tpla_status tpla_decode_shard(const tpla_decode_args* a, void* workspace, size_t
   m.d_s = a->d_s;
   m.ws_o = p.ws_o;
   m.ws_lse = p.ws_lse;
+  m.blk_cols = (decode_path(a) == Path::kStream &&
+                tpla::decode_latsplit_supported(a->heads, a->d_s, a->d_r, a->block_size))
+                   ? tpla::decode_latsplit_partial_block()
+                   : 0;
   m.out = a->out;
   m.out_bf16 = a->out_dtype == TPLA_BF16;
   m.out_sb = a->out_stride_b;

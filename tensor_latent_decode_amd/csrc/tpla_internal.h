@@ -55,8 +55,18 @@ struct DecodeParams {
   float* ws_lse;                // [splits, batch, heads]
 };
 
+// Split outputs are either float32 [splits, batch, heads, d_s] at ws_o, or
+// fp16 at the same address with one float scale per (split, b, h, block of
+// blk_cols columns) at ws_o + fp16_partials_scale_offset(...) bytes.
+__host__ __device__ inline size_t fp16_partials_scale_offset(int splits, int batch, int heads,
+                                                              int d_s) {
+  const size_t n = static_cast<size_t>(splits) * batch * heads * d_s * 2;
+  return (n + 255) & ~static_cast<size_t>(255);
+}
+
 struct MergeParams {
   int splits, batch, heads, d_s;
+  int blk_cols;                 // 0: float32 partials; else fp16 partials, scale per blk_cols
   const float* ws_o;
   const float* ws_lse;
   void* out;
@@ -88,6 +98,7 @@ int decode_stream_groups_per_cu(int heads, int d_s, int d_r);
 hipError_t launch_decode_latsplit(const DecodeParams& p, hipStream_t s);
 bool decode_latsplit_supported(int heads, int d_s, int d_r, int block_size);
 int decode_latsplit_max_chunk();   // tokens per split the latent-split kernel accepts
+int decode_latsplit_partial_block();   // columns per scale of its fp16 split outputs
 hipError_t launch_decode_generic(const DecodeParams& p, int is_bf16, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_combine(const PartPtrs& parts, int part_bf16, int tp, int batch, int heads,
