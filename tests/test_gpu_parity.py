@@ -236,6 +236,32 @@ def test_decode_bf16_ragged_parity(shape, bs, splits):
             assert np.max(np.abs(host_f64(lses[g])[b] - l)) <= 2e-2
 
 
+@pytest.mark.parametrize("shape", SHAPES[:3])
+@pytest.mark.parametrize("bs", [64, 16])
+def test_decode_bf16_late_score_spike(shape, bs):
+    """A token deep inside the first split scores far above everything before
+    it (head 0: about 2500 raw, ~260 in base-2 exponent units), so a softmax
+    that kept the first tile's max as its reference would overflow.  Every
+    head must still match the oracle on its own scale."""
+    H, d_c, tp, d_r = shape
+    from dataclasses import replace
+    cfg = replace(CONFIGS["dsv3_4k"], heads=H, d_c=d_c, tp=tp, d_r=d_r, scale=1 / math.sqrt(192.0))
+    case = make_case(cfg, batch=2, ctx=1500, block_size=bs, seed=70 + H + bs)
+    d_s = d_c // tp
+    q0 = as_f64(case.q_latent[0, 0])                      # head 0's query, whole latent
+    k = 2500.0 / (cfg.scale * float(np.mean([q0[g * d_s:(g + 1) * d_s] @ q0[g * d_s:(g + 1) * d_s]
+                                               for g in range(tp)])))
+    from tensor_latent_decode_amd.inputs import bf16_bits
+    case.hist_latent[700] = bf16_bits((k * q0).astype(np.float32))   # sequence 0, position 700
+    gc = GpuCase(case)
+    combined, outs, _ = run_step(gc, hadamard=False, num_splits=1)
+    got = host_f64(combined)
+    for b in range(2):
+        ref, _ = oracle_step(case, b, tp, hadamard=False)
+        for h in range(H):
+            assert rel_err(got[b, h], ref[h]) <= TOL_BF16, (b, h)
+
+
 @pytest.mark.parametrize("lens", [[1, 2, 63, 64], [65, 127, 128, 129], [4096, 1, 1000, 3]])
 def test_decode_bf16_edge_lengths(lens):
     cases = [make_case(CONFIGS["dsv3_4k"], batch=1, ctx=L, seed=41 + i)
