@@ -4,10 +4,11 @@
     python bench.py [--steps K] [--warmup W] [--workload dsv3_32k]
 
 A step is the whole decode hot path over one batch, with every input already
-resident in HBM: rotate the absorbed query and the new token's latent
-(tpla_hadamard_latent), append the new row to the shard cache
-(tpla_append_kv), decode the shard (tpla_decode_shard: split-K attention and
-log-sum-exp merge) and combine the shard outputs (tpla_combine_shards).
+resident in HBM: rotate the absorbed query and the new token's latent and
+append the new row to the shard caches (tpla_rotate_append: one launch for
+what tpla_hadamard_latent and tpla_append_kv do separately), decode the shard
+(tpla_decode_shard: split-K attention and log-sum-exp merge) and combine the
+shard outputs (tpla_combine_shards).
 The default workload is the DeepSeek-V3-shaped shard at 32K context
 (B=16, H=128, d_c=512 split TP=2 -> d_s=256, d_r=64, paged blocks of 64 with
 a permuted block table); `--workload ragged_tp2` runs both shards of the
@@ -213,7 +214,6 @@ def main():
     del hist_lat, hist_rope, hist_seq, hist_pos
     maxlen = int(case.seq_lens.max())
     q_rot = torch.empty((B, H, d_c), dtype=torch.bfloat16, device="cuda")
-    new_rot = torch.empty((B, d_c), dtype=torch.bfloat16, device="cuda")
     outs = [torch.empty((B, H, d_s), dtype=torch.float32, device="cuda") for _ in shards]
     lses = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in shards]
     combined = torch.empty((B, H, len(shards) * d_s), dtype=torch.float32, device="cuda")
@@ -229,11 +229,9 @@ def main():
                           workspace=workspace)
 
     def step(r):
-        tpla.hadamard_latent(q_raw, out=q_rot)
-        tpla.hadamard_latent(new_raw, out=new_rot)
+        tpla.rotate_append(q_raw, q_rot, new_raw, new_rope, new_seq, new_pos, caches[r], bt,
+                           first_shard=shards[0])
         for i, g in enumerate(shards):
-            tpla.append_kv(caches[r][i], bt, new_seq, new_pos, new_rot[:, g * d_s:(g + 1) * d_s],
-                           new_rope)
             decode(r, i, g)
         tpla.combine_shards(outs, out=combined)
 

@@ -123,6 +123,65 @@ tpla_status tpla_append_kv(void* cache, tpla_dtype cache_dtype, int32_t num_bloc
                            void* stream);
 
 /*
+ * Arguments of tpla_rotate_append.
+ */
+typedef struct tpla_rotate_append_args {
+  int32_t n;                   /* latent width d_c: power of two, 64 .. 4096    */
+  const void* q;               /* device, q_rows absorbed-query rows of n       */
+  tpla_dtype q_dtype;
+  int64_t q_row_stride;        /* elements                                      */
+  void* q_out;                 /* device, rotated query rows (may equal q)      */
+  tpla_dtype q_out_dtype;
+  int64_t q_out_row_stride;
+  int64_t q_rows;              /* 0: no query rows                              */
+  const void* latent;          /* device, n_rows new-token latent rows of n,    */
+                               /*   unrotated                                   */
+  const void* rope;            /* device, n_rows rope rows of d_r (NULL if 0)   */
+  tpla_dtype src_dtype;        /* of latent, rope and latent_out                */
+  int64_t latent_row_stride;
+  int64_t rope_row_stride;
+  void* latent_out;            /* device or NULL: the rotated latent rows       */
+  int64_t latent_out_row_stride;
+  int32_t n_rows;              /* 0: no new rows                                */
+  const int32_t* row_seq;      /* device int32 [n_rows]                         */
+  const int32_t* row_pos;      /* device int32 [n_rows]                         */
+  void* const* caches;         /* HOST array of n_caches device shard caches    */
+  int32_t n_caches;            /* 0 .. 16                                       */
+  int32_t first_shard;         /* caches[c] holds latent shard first_shard + c  */
+  tpla_dtype cache_dtype;
+  int32_t num_blocks;          /* per cache, as tpla_append_kv                  */
+  int32_t block_size;
+  int32_t d_s;
+  int32_t d_r;
+  const int32_t* block_table;  /* device int32 [batch, max_blocks_per_seq]      */
+  int32_t max_blocks_per_seq;
+  int32_t batch;
+} tpla_rotate_append_args;
+
+/*
+ * tpla_rotate_append: the rotation of the query, the rotation of the new
+ * token's latent and its paged append (tpla_hadamard_latent twice and
+ * tpla_append_kv once per cache) in one launch, with identical results.
+ *
+ * TPLA rotates the absorbed query and the latent by an orthogonal transform
+ * before slicing them (TPLA abstract; edgentiq blog, "How TPLA Works: Smart
+ * Slicing and Reparameterization"), and each device caches only its latent
+ * slice plus the rope (TPLA abstract).  With Hn = H_n / sqrt(n):
+ *     q_out[r, :]      = q[r, :] . Hn                      r < q_rows
+ *     c~               = latent[t, :] . Hn                 t < n_rows
+ *     latent_out[t, :] = c~                                (if latent_out)
+ *     caches[c][slot]  = [ c~[(first_shard+c)*d_s : +d_s] || rope[t, :] ]
+ * with slot as in tpla_append_kv (rows with an out-of-range sequence,
+ * position or block id are skipped).  Arithmetic and rounding are those of
+ * tpla_hadamard_latent (float32, one round-to-nearest-even to the output
+ * dtype); a rope of the cache's type is copied bit for bit.
+ * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE (n not a power of two in
+ * [64, 4096], strides shorter than a row, shards beyond n, n_caches outside
+ * [0, 16], negative counts), TPLA_ERR_DTYPE.
+ */
+tpla_status tpla_rotate_append(const tpla_rotate_append_args* args, void* stream);
+
+/*
  * Arguments of one shard's decode step (see tpla_decode_shard).
  */
 typedef struct tpla_decode_args {

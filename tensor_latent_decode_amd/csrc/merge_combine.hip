@@ -16,14 +16,6 @@
 namespace tpla {
 namespace {
 
-// One thread per (b, h, 4 consecutive columns); a wavefront covers 256
-// columns of one or more (b, h) rows, so the lse reads are broadcasts and the
-// partial reads are contiguous float4 runs.  The split loop is unrolled by 8
-// with all loads issued before they are used; splits without tokens get
-// weight 0 by a select (their workspace rows are read but never trusted).
-// Workgroup n handles items ((n % 8) * per_xcd + n / 8) * 256 ..., i.e.
-// sequences are spread over the XCDs in the same order as the split-K
-// kernel placed them.
 // Four consecutive columns of split s's output for row bh (float32 or
 // scaled fp16 partials).
 template <bool kFp16Parts>
@@ -49,6 +41,14 @@ __device__ __forceinline__ float4 load_part(const MergeParams& p, int s, int64_t
   }
 }
 
+// One thread per (b, h, 4 consecutive columns); a wavefront covers 256
+// columns of one or more (b, h) rows, so the lse reads are broadcasts and the
+// partial reads are contiguous runs.  Splits are taken 16 at a time with a
+// running max (all of a chunk's loads are in flight together); splits
+// without tokens get weight 0 by a select (their workspace rows are read but
+// never trusted).  Workgroup n handles items ((n % 8) * per_xcd + n / 8) *
+// 256 ..., i.e. sequences are spread over the XCDs in the same order as the
+// split-K kernel placed them.
 template <bool kBf16Out, bool kFp16Parts>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_items, int per_xcd) {
   const int n = blockIdx.x;
@@ -62,39 +62,52 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_ite
   const bool vec = (p.d_s & 3) == 0;
   const int64_t stride_s = static_cast<int64_t>(p.batch) * p.heads;
   const float* lse_in = p.ws_lse + bh;
-  float mx = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, lse_in[s * stride_s]);
   const int b = static_cast<int>(bh / p.heads);
   const int h = static_cast<int>(bh % p.heads);
   const int64_t obase = b * p.out_sb + h * p.out_sh + col;
+  // Online over chunks of 16 splits: every load of a chunk is issued before
+  // any is used (one memory round trip for up to 16 splits).
+  constexpr int kC = 16;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  float lse = -INFINITY;
-  if (mx != -INFINITY) {
-    float tot = 0.f;
-    for (int s0 = 0; s0 < p.splits; s0 += 8) {
-      float w[8];
-      float4 v[8];
+  float m = -INFINITY, tot = 0.f;
+  for (int s0 = 0; s0 < p.splits; s0 += kC) {
+    float l[kC];
+    float4 v[kC];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int s = min(s0 + u, p.splits - 1);
-        const float l = lse_in[s * stride_s];
-        w[u] = (s0 + u < p.splits && l != -INFINITY) ? __expf(l - mx) : 0.f;
-        v[u] = load_part<kFp16Parts>(p, s, bh, col, ncol, vec, stride_s);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool use = w[u] != 0.f;
-        tot += w[u];
-        acc[0] += use ? w[u] * v[u].x : 0.f;
-        acc[1] += use ? w[u] * v[u].y : 0.f;
-        acc[2] += use ? w[u] * v[u].z : 0.f;
-        acc[3] += use ? w[u] * v[u].w : 0.f;
-      }
+    for (int u = 0; u < kC; ++u) {
+      const int s = min(s0 + u, p.splits - 1);
+      l[u] = lse_in[s * stride_s];
+      v[u] = load_part<kFp16Parts>(p, s, bh, col, ncol, vec, stride_s);
     }
+    float cm = m;
+#pragma unroll
+    for (int u = 0; u < kC; ++u) {
+      if (s0 + u >= p.splits) l[u] = -INFINITY;
+      cm = fmaxf(cm, l[u]);
+    }
+    if (cm == -INFINITY) continue;              // no tokens so far
+    const float r = __expf(m - cm);             // 0 while m is still -inf
+    tot *= r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] *= r;
+#pragma unroll
+    for (int u = 0; u < kC; ++u) {
+      const bool use = l[u] != -INFINITY;       // empty splits: weight 0, o never used
+      const float w = use ? __expf(l[u] - cm) : 0.f;
+      tot += w;
+      acc[0] += use ? w * v[u].x : 0.f;
+      acc[1] += use ? w * v[u].y : 0.f;
+      acc[2] += use ? w * v[u].z : 0.f;
+      acc[3] += use ? w * v[u].w : 0.f;
+    }
+    m = cm;
+  }
+  float lse = -INFINITY;
+  if (m != -INFINITY) {
     const float inv = 1.0f / tot;
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] *= inv;
-    lse = mx + __logf(tot);
+    lse = m + __logf(tot);
   }
   const bool out_vec = vec && ((reinterpret_cast<uintptr_t>(static_cast<float*>(p.out) + obase) & 15) == 0);
   if (out_vec && !kBf16Out) {

@@ -185,7 +185,7 @@ const char* tpla_status_string(tpla_status s) {
 
 const char* tpla_last_error(void) { return g_err; }
 
-int32_t tpla_version(void) { return 100; }
+int32_t tpla_version(void) { return 200; }
 
 tpla_status tpla_hadamard_latent(const void* x, tpla_dtype x_dtype, int64_t x_row_stride, void* y,
                                  tpla_dtype y_dtype, int64_t y_row_stride, int64_t rows, int32_t n,
@@ -227,6 +227,78 @@ tpla_status tpla_append_kv(void* cache, tpla_dtype cache_dtype, int32_t num_bloc
                           latent_row_stride, rope, rope_row_stride, src_dtype == TPLA_BF16,
                           static_cast<hipStream_t>(stream)),
       "append launch");
+}
+
+tpla_status tpla_rotate_append(const tpla_rotate_append_args* a, void* stream) {
+  if (a == nullptr) return fail(TPLA_ERR_NULL, "args is NULL");
+  if (!valid_dtype(a->q_dtype) || !valid_dtype(a->q_out_dtype) || !valid_dtype(a->src_dtype) ||
+      !valid_dtype(a->cache_dtype))
+    return fail(TPLA_ERR_DTYPE, "dtypes must be TPLA_FP32 or TPLA_BF16");
+  const int n = a->n;
+  if (!is_pow2(n) || n < 64 || n > 4096)
+    return fail(TPLA_ERR_SHAPE, "n=%d must be a power of two in [64, 4096]", n);
+  if (a->q_rows < 0 || a->n_rows < 0) return fail(TPLA_ERR_SHAPE, "q_rows and n_rows must be >= 0");
+  if (a->n_caches < 0 || a->n_caches > tpla::kMaxTp)
+    return fail(TPLA_ERR_SHAPE, "n_caches must be in [0, %d]", tpla::kMaxTp);
+  if (a->q_rows > 0) {
+    if (a->q == nullptr || a->q_out == nullptr) return fail(TPLA_ERR_NULL, "q and q_out are required");
+    if (a->q_row_stride < n || a->q_out_row_stride < n)
+      return fail(TPLA_ERR_SHAPE, "query row strides must be >= n");
+  }
+  if (a->n_rows > 0) {
+    if (a->latent == nullptr) return fail(TPLA_ERR_NULL, "latent is required");
+    if (a->latent_row_stride < n || (a->latent_out != nullptr && a->latent_out_row_stride < n))
+      return fail(TPLA_ERR_SHAPE, "latent row strides must be >= n");
+    if (a->n_caches > 0) {
+      if (a->num_blocks < 1 || a->block_size < 1 || a->d_s < 1 || a->d_r < 0 ||
+          a->max_blocks_per_seq < 1 || a->batch < 1)
+        return fail(TPLA_ERR_SHAPE, "non-positive cache size");
+      if (a->first_shard < 0 ||
+          static_cast<int64_t>(a->first_shard + a->n_caches) * a->d_s > n)
+        return fail(TPLA_ERR_SHAPE, "shards %d..%d of width %d exceed n=%d", a->first_shard,
+                    a->first_shard + a->n_caches - 1, a->d_s, n);
+      if (a->d_r > 0 && (a->rope == nullptr || a->rope_row_stride < a->d_r))
+        return fail(a->rope == nullptr ? TPLA_ERR_NULL : TPLA_ERR_SHAPE,
+                    "rope is required with a row stride >= d_r");
+      if (a->caches == nullptr || a->block_table == nullptr || a->row_seq == nullptr ||
+          a->row_pos == nullptr)
+        return fail(TPLA_ERR_NULL, "caches, block_table, row_seq and row_pos are required");
+      for (int c = 0; c < a->n_caches; ++c)
+        if (a->caches[c] == nullptr) return fail(TPLA_ERR_NULL, "caches[%d] is NULL", c);
+    }
+  }
+  if (a->q_rows == 0 && a->n_rows == 0) return ok();
+  tpla::RotateAppendParams p{};
+  p.q = a->q;
+  p.qs = a->q_row_stride;
+  p.q_out = a->q_out;
+  p.qos = a->q_out_row_stride;
+  p.q_rows = a->q_rows;
+  p.q_bf16 = a->q_dtype == TPLA_BF16;
+  p.q_out_bf16 = a->q_out_dtype == TPLA_BF16;
+  p.lat = a->latent;
+  p.ls = a->latent_row_stride;
+  p.rope = a->rope;
+  p.rs = a->rope_row_stride;
+  p.lat_out = a->latent_out;
+  p.los = a->latent_out_row_stride;
+  p.lat_bf16 = a->src_dtype == TPLA_BF16;
+  p.n_rows = a->n_rows;
+  p.row_seq = a->row_seq;
+  p.row_pos = a->row_pos;
+  p.n_caches = a->n_rows > 0 ? a->n_caches : 0;
+  for (int c = 0; c < p.n_caches; ++c) p.caches.p[c] = a->caches[c];
+  p.first_shard = a->first_shard;
+  p.cache_bf16 = a->cache_dtype == TPLA_BF16;
+  p.num_blocks = a->num_blocks;
+  p.block_size = a->block_size;
+  p.d_s = a->d_s;
+  p.d_r = a->d_r;
+  p.max_blocks = a->max_blocks_per_seq;
+  p.batch = a->batch;
+  p.bt = a->block_table;
+  return hip_status(tpla::launch_rotate_append(p, n, static_cast<hipStream_t>(stream)),
+                    "rotate/append launch");
 }
 
 tpla_status tpla_decode_workspace_size(const tpla_decode_args* args, size_t* bytes) {

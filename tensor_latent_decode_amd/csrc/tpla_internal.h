@@ -79,10 +79,39 @@ constexpr int kMaxTp = 16;
 struct PartPtrs {
   const void* p[kMaxTp];
 };
+struct CachePtrs {
+  void* p[kMaxTp];
+};
+
+// Rotation of query rows and new latent rows, and the paged append of the
+// new rows' shard slices (one launch).
+struct RotateAppendParams {
+  const void* q;
+  int64_t qs;
+  void* q_out;
+  int64_t qos;
+  int64_t q_rows;
+  int q_bf16, q_out_bf16;
+  const void* lat;              // new latent rows, n wide, unrotated
+  int64_t ls;
+  const void* rope;             // same dtype as lat
+  int64_t rs;
+  void* lat_out;                // optional rotated copy (lat's dtype)
+  int64_t los;
+  int lat_bf16;
+  int n_rows;
+  const int32_t* row_seq;
+  const int32_t* row_pos;
+  CachePtrs caches;
+  int n_caches, first_shard, cache_bf16;
+  int num_blocks, block_size, d_s, d_r, max_blocks, batch;
+  const int32_t* bt;
+};
 
 // Launchers (return the launch status; they do not synchronise).
 hipError_t launch_hadamard(const void* x, int x_bf16, int64_t xs, void* y, int y_bf16, int64_t ys,
                            int64_t rows, int n, hipStream_t s);
+hipError_t launch_rotate_append(const RotateAppendParams& p, int n, hipStream_t s);
 hipError_t launch_append(void* cache, int cache_bf16, int num_blocks, int block_size, int d_s,
                          int d_r, const int32_t* bt, int max_blocks, int batch,
                          const int32_t* row_seq, const int32_t* row_pos, int n_rows,

@@ -51,6 +51,25 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class RotateAppendArgs(ctypes.Structure):
+    """Mirror of tpla_rotate_append_args (include/tpla.h)."""
+    _fields_ = [
+        ("n", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("q_dtype", ctypes.c_int), ("q_row_stride", ctypes.c_int64),
+        ("q_out", ctypes.c_void_p), ("q_out_dtype", ctypes.c_int),
+        ("q_out_row_stride", ctypes.c_int64), ("q_rows", ctypes.c_int64),
+        ("latent", ctypes.c_void_p), ("rope", ctypes.c_void_p), ("src_dtype", ctypes.c_int),
+        ("latent_row_stride", ctypes.c_int64), ("rope_row_stride", ctypes.c_int64),
+        ("latent_out", ctypes.c_void_p), ("latent_out_row_stride", ctypes.c_int64),
+        ("n_rows", ctypes.c_int32), ("row_seq", ctypes.c_void_p), ("row_pos", ctypes.c_void_p),
+        ("caches", ctypes.POINTER(ctypes.c_void_p)), ("n_caches", ctypes.c_int32),
+        ("first_shard", ctypes.c_int32), ("cache_dtype", ctypes.c_int),
+        ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32), ("d_s", ctypes.c_int32),
+        ("d_r", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+        ("max_blocks_per_seq", ctypes.c_int32), ("batch", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -71,8 +90,9 @@ def lib() -> ctypes.CDLL:
     L.tpla_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(sz)]
     L.tpla_decode_shard.argtypes = [ctypes.POINTER(DecodeArgs), vp, sz, vp]
     L.tpla_combine_shards.argtypes = [ctypes.POINTER(vp), dt, i32, i32, i32, i32, vp, dt, i32, vp]
+    L.tpla_rotate_append.argtypes = [ctypes.POINTER(RotateAppendArgs), vp]
     for f in ("tpla_hadamard_latent", "tpla_append_kv", "tpla_decode_workspace_size",
-              "tpla_decode_shard", "tpla_combine_shards"):
+              "tpla_decode_shard", "tpla_combine_shards", "tpla_rotate_append"):
         getattr(L, f).restype = ctypes.c_int
     L.tpla_status_string.argtypes = [ctypes.c_int]
     L.tpla_status_string.restype = ctypes.c_char_p
@@ -177,6 +197,76 @@ def append_kv(cache: torch.Tensor, block_table: torch.Tensor, row_seq: torch.Ten
                                 None if rope is None else rope.data_ptr(),
                                 0 if rope is None else (rope.stride(0) if n_rows > 1 else d_r),
                                 _dt(latent), _stream(cache)))
+
+
+def rotate_append(q: Optional[torch.Tensor], q_out: Optional[torch.Tensor],
+                  latent: Optional[torch.Tensor], rope: Optional[torch.Tensor],
+                  row_seq: Optional[torch.Tensor] = None, row_pos: Optional[torch.Tensor] = None,
+                  caches: Sequence[torch.Tensor] = (), block_table: Optional[torch.Tensor] = None,
+                  first_shard: int = 0, latent_out: Optional[torch.Tensor] = None,
+                  batch: Optional[int] = None) -> None:
+    """One launch: q_out = q . H_n/sqrt(n) over the last dim; the new latent
+    rows rotated the same way (into latent_out if given) and their shard
+    slices first_shard, first_shard+1, ... appended with the rope into
+    `caches` (each [num_blocks, block_size, d_s + d_r])."""
+    _gpu(q, q_out, latent, rope, row_seq, row_pos, block_table, latent_out, *caches)
+    a = RotateAppendArgs()
+    n = None
+    if q is not None:
+        if q_out is None or q_out.shape != q.shape:
+            raise ValueError("q_out must have q's shape")
+        rows, n, qs = _rows(q)
+        _, _, qos = _rows(q_out)
+        a.q, a.q_dtype, a.q_row_stride = q.data_ptr(), _dt(q), qs
+        a.q_out, a.q_out_dtype, a.q_out_row_stride = q_out.data_ptr(), _dt(q_out), qos
+        a.q_rows = rows
+    if rope is not None and rope.shape[-1] == 0:
+        rope = None
+    keep = []
+    if latent is not None:
+        if latent.dim() != 2 or latent.stride(-1) != 1:
+            raise ValueError("latent must be [n_rows, n] with contiguous rows")
+        n_rows, nl = latent.shape
+        if n is not None and nl != n:
+            raise ValueError("latent and q rows must have the same width")
+        n = nl
+        a.latent, a.src_dtype = latent.data_ptr(), _dt(latent)
+        a.latent_row_stride = latent.stride(0) if n_rows > 1 else n
+        a.n_rows = n_rows
+        if rope is not None:
+            if rope.dtype != latent.dtype or rope.stride(-1) != 1:
+                raise ValueError("rope must share latent's dtype and have contiguous rows")
+            a.rope, a.d_r = rope.data_ptr(), rope.shape[-1]
+            a.rope_row_stride = rope.stride(0) if n_rows > 1 else rope.shape[-1]
+        if latent_out is not None:
+            if latent_out.shape != latent.shape or latent_out.dtype != latent.dtype:
+                raise ValueError("latent_out must match latent")
+            a.latent_out = latent_out.data_ptr()
+            a.latent_out_row_stride = latent_out.stride(0) if n_rows > 1 else n
+        if caches:
+            if block_table is None or row_seq is None or row_pos is None:
+                raise ValueError("caches need block_table, row_seq and row_pos")
+            for t in (block_table, row_seq, row_pos):
+                if t.dtype != torch.int32 or not t.is_contiguous():
+                    raise ValueError("block_table, row_seq, row_pos must be contiguous int32")
+            c0 = caches[0]
+            num_blocks, bs, width = c0.shape
+            for c in caches:
+                if c.shape != c0.shape or c.dtype != c0.dtype or not c.is_contiguous():
+                    raise ValueError("caches must be alike and contiguous")
+            arr = (ctypes.c_void_p * len(caches))(*[c.data_ptr() for c in caches])
+            keep.append(arr)
+            a.caches = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+            a.n_caches, a.first_shard, a.cache_dtype = len(caches), first_shard, _dt(c0)
+            a.num_blocks, a.block_size, a.d_s = num_blocks, bs, width - a.d_r
+            a.block_table, a.max_blocks_per_seq = block_table.data_ptr(), block_table.shape[1]
+            a.batch = block_table.shape[0] if batch is None else batch
+            a.row_seq, a.row_pos = row_seq.data_ptr(), row_pos.data_ptr()
+    if n is None:
+        return
+    a.n = n
+    dev_t = q if q is not None else latent
+    _check("tpla_rotate_append", lib().tpla_rotate_append(ctypes.byref(a), _stream(dev_t)))
 
 
 def make_decode_args(q_latent: torch.Tensor, q_rope: Optional[torch.Tensor], cache: torch.Tensor,

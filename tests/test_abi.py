@@ -18,7 +18,7 @@ def test_exports_every_declared_function():
     names = tpla.header_functions()
     assert {"tpla_hadamard_latent", "tpla_append_kv", "tpla_decode_workspace_size",
             "tpla_decode_shard", "tpla_combine_shards", "tpla_status_string",
-            "tpla_last_error", "tpla_version"} <= set(names)
+            "tpla_last_error", "tpla_version", "tpla_rotate_append"} <= set(names)
     raw = ctypes.CDLL(tpla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -26,7 +26,7 @@ def test_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = tpla.lib()
-    assert tpla.version() == 100
+    assert tpla.version() == 200
     for code in range(8):
         assert L.tpla_status_string(code)
     assert L.tpla_status_string(99) == b"unknown status"
@@ -70,6 +70,46 @@ def test_append_argument_checks():
     args[11] = 0
     args[0] = None
     assert L.tpla_append_kv(*args) == 0     # zero rows is a no-op
+
+
+def _rot_args():
+    a = tpla.RotateAppendArgs()
+    a.n = 512
+    a.q, a.q_dtype, a.q_row_stride = FAKE, 1, 512
+    a.q_out, a.q_out_dtype, a.q_out_row_stride = FAKE, 1, 512
+    a.q_rows = 2048
+    a.latent, a.rope, a.src_dtype = FAKE, FAKE, 1
+    a.latent_row_stride, a.rope_row_stride = 512, 64
+    a.n_rows, a.row_seq, a.row_pos = 16, FAKE, FAKE
+    caches = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    a.caches = ctypes.cast(caches, ctypes.POINTER(ctypes.c_void_p))
+    a.n_caches, a.first_shard, a.cache_dtype = 2, 0, 1
+    a.num_blocks, a.block_size, a.d_s, a.d_r = 100, 64, 256, 64
+    a.block_table, a.max_blocks_per_seq, a.batch = FAKE, 50, 16
+    return a, caches
+
+
+def test_rotate_append_argument_checks():
+    L = tpla.lib()
+    def call(a):
+        return L.tpla_rotate_append(ctypes.byref(a), None)
+    for field, value, code in [("n", 48, 2), ("n", 32, 2), ("n", 8192, 2), ("q_dtype", 3, 4),
+                               ("cache_dtype", 9, 4), ("q_row_stride", 100, 2),
+                               ("latent_row_stride", 256, 2), ("rope_row_stride", 10, 2),
+                               ("first_shard", 1, 2), ("n_caches", 17, 2), ("q_rows", -1, 2),
+                               ("n_rows", -2, 2), ("q", None, 1), ("latent", None, 1),
+                               ("rope", None, 1), ("block_table", None, 1), ("row_seq", None, 1)]:
+        a, keep = _rot_args()
+        setattr(a, field, value)
+        _fails(call(a), code)
+    a, keep = _rot_args()
+    keep[1] = None                                   # caches[1] is NULL
+    _fails(call(a), 1)
+    a, keep = _rot_args()
+    a.q_rows, a.n_rows = 0, 0
+    a.q = a.latent = None
+    assert call(a) == 0                              # nothing to do
+    _fails(L.tpla_rotate_append(None, None), 1)
 
 
 def _args(**kw):

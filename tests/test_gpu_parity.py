@@ -123,6 +123,84 @@ def test_append_skips_out_of_range_rows():
 
 
 # --------------------------------------------------------------------------
+# Fused rotation + append (one launch) against the separate calls and the oracle
+# --------------------------------------------------------------------------
+
+def _bits(t):
+    h = host_bits(t)
+    return h.view(np.uint32) if h.dtype == np.float32 else h
+
+
+@pytest.mark.parametrize("cfg,bs,first,count", [("tiny_fp32", 16, 0, 2), ("dsv3_4k", 64, 0, 2),
+                                                ("dsv3_4k", 16, 1, 1), ("kimi_k2_32k", 64, 0, 4),
+                                                ("kimi_k2_32k", 64, 2, 2)])
+def test_rotate_append_matches_separate_calls(cfg, bs, first, count):
+    case = make_case(CONFIGS[cfg], batch=3, ctx=(30, 200), block_size=bs, seed=17,
+                     heads=min(CONFIGS[cfg].heads, 32))
+    gc = GpuCase(case)
+    d_s = case.cfg.d_s
+    shards = list(range(first, first + count))
+    # separate calls: rotate query, rotate new latent, append per shard
+    q_ref = tpla.hadamard_latent(gc.q_latent)
+    new_ref = tpla.hadamard_latent(gc.new_latent)
+    ref_caches = []
+    for g in shards:
+        c = gc.prefill(g, d_s)
+        tpla.append_kv(c, gc.bt, gc.new_seq, gc.new_pos, new_ref[:, g * d_s:(g + 1) * d_s],
+                       gc.new_rope)
+        ref_caches.append(c)
+    # one launch
+    q_out = torch.empty_like(gc.q_latent)
+    new_out = torch.empty_like(gc.new_latent)
+    caches = [gc.prefill(g, d_s) for g in shards]
+    tpla.rotate_append(gc.q_latent, q_out, gc.new_latent, gc.new_rope, gc.new_seq, gc.new_pos,
+                       caches, gc.bt, first_shard=first, latent_out=new_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(q_out), _bits(q_ref))
+    assert np.array_equal(_bits(new_out), _bits(new_ref))
+    for c, r in zip(caches, ref_caches):
+        assert np.array_equal(_bits(c), _bits(r))
+    # and the oracle: rotated query and the appended rows
+    q64 = as_f64(case.q_latent)
+    tol = TOL_BF16 if case.cfg.dtype == "bf16" else TOL_FP32
+    assert rel_err(host_f64(q_out), oracle.fwht(q64)) <= tol
+    new64 = oracle.fwht(as_f64(case.new_latent))
+    for g, c in zip(shards, caches):
+        got = host_f64(c)
+        for b in range(3):
+            p = int(case.new_pos[b])
+            row = got[int(case.block_table[b, p // bs]), p % bs]
+            assert rel_err(row[:d_s], new64[b, g * d_s:(g + 1) * d_s]) <= tol
+            want = case.new_rope[b] if case.cfg.dtype == "bf16" else case.new_rope[b].view(np.uint32)
+            assert np.array_equal(_bits(c)[int(case.block_table[b, p // bs]), p % bs, d_s:], want)
+
+
+def test_rotate_append_fp32_sources_and_skipped_rows():
+    case = make_case(CONFIGS["dsv3_4k"], batch=4, ctx=(10, 80), seed=19, heads=32)
+    gc = GpuCase(case)
+    q32, new32, rope32 = gc.q_latent.float(), gc.new_latent.float(), gc.new_rope.float()
+    q_out = torch.empty_like(gc.q_latent)                      # fp32 in, bf16 out
+    seq = torch.tensor([0, -1, 2, 3], dtype=torch.int32, device="cuda")
+    pos = gc.new_pos.clone()
+    pos[3] = case.max_blocks * 64                               # past the table: skipped
+    caches = [gc.prefill(g, 256) for g in range(2)]
+    before = [_bits(c).copy() for c in caches]
+    tpla.rotate_append(q32, q_out, new32, rope32, seq, pos, caches, gc.bt)
+    ref_q = tpla.hadamard_latent(q32, out_dtype=torch.bfloat16)
+    new_rot = tpla.hadamard_latent(new32)                      # fp32
+    ref = [c.clone() for c in [gc.prefill(g, 256) for g in range(2)]]
+    for g in range(2):
+        tpla.append_kv(ref[g], gc.bt, seq[[0, 2]], pos[[0, 2]], new_rot[[0, 2], g * 256:(g + 1) * 256],
+                       rope32[[0, 2]])
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(q_out), _bits(ref_q))
+    for g in range(2):
+        got = _bits(caches[g])
+        assert np.array_equal(got, _bits(ref[g]))
+        assert int(np.sum(got != before[g])) > 0
+
+
+# --------------------------------------------------------------------------
 # Combine (bit-exact placement)
 # --------------------------------------------------------------------------
 
