@@ -14,7 +14,8 @@ The default workload is the DeepSeek-V3-shaped shard at 32K context
 a permuted block table); `--workload ragged_tp2` runs both shards of the
 ragged TP=2 step in turn.
 
-Steps are replayed from HIP graphs (one per cache replica).  Replicas rotate
+Steps are replayed from HIP graphs (one holding several steps, cache replicas
+in turn, plus one per replica for a remainder).  Replicas rotate
 so that the caches read by consecutive steps together exceed the 256 MB
 Infinity Cache (the next layer's cache would evict it in a real model).
 
@@ -49,8 +50,8 @@ MALL_BYTES = 256 * 2 ** 20      # Infinity Cache
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv3_32k",
                     choices=["dsv3_32k", "kimi_k2_32k", "ragged_tp2", "dsv3_4k"])
     ap.add_argument("--mode", default="step", choices=["step", "decode", "copy"])
@@ -248,6 +249,14 @@ def main():
         with torch.cuda.graph(gr, stream=stream):
             step(r)
         graphs.append(gr)
+    # one graph holding several steps, replicas in turn (a model's whole decode
+    # step, all layers, would be one graph; a replay costs a fixed host and
+    # queue overhead that a one-layer graph would otherwise carry alone)
+    per_cycle = replicas * max(1, -(-8 // replicas))
+    cycle = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cycle, stream=stream):
+        for k in range(per_cycle):
+            step(k % replicas)
     # graph of back-to-back decode launches (replicas rotating) for kernel timing
     dec_graph = torch.cuda.CUDAGraph()
     n_dec = max(args.decode_launches, replicas)
@@ -273,8 +282,11 @@ def main():
         return
 
     torch.cuda.synchronize()
+    full, rest = divmod(args.steps, per_cycle)
     ev0.record()
-    for k in range(args.steps):
+    for _ in range(full):
+        cycle.replay()
+    for k in range(rest):
         graphs[k % replicas].replay()
     ev1.record()
     torch.cuda.synchronize()
