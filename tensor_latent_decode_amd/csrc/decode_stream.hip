@@ -51,6 +51,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+
+// Scalar (constant address space) read of a wave-uniform int32: as a plain
+// load it would be a vector load, and its wait would also wait for every
+// tile copy in flight.
+__device__ __forceinline__ int scalar_load(const int32_t* p) { return *(const const_i32_t*)p; }
 
 constexpr int kTile = 64;
 constexpr float kRescale = 64.0f;   // base-2 headroom of P above the reference
@@ -128,7 +134,7 @@ void decode_stream_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   const int l31 = lane & 31, half = lane >> 5;
   const int head = hg * (32 * NW) + wave * 32 + l31;
 
-  int L = p.seq_lens[b];
+  int L = scalar_load(p.seq_lens + b);
   L = max(0, min(L, min(p.max_seq_len, p.max_blocks * p.block_size)));
   const int t0 = split * p.chunk;
   const int t1 = min(L, t0 + p.chunk);
@@ -174,7 +180,7 @@ void decode_stream_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   auto copy_tile = [&](int t, int kb) {
     const int tb = t0 + t * kTile;
     const int nvalid = min(kTile, t1 - tb);
-    const int page = bt_row[tb / bs];
+    const int page = scalar_load(bt_row + tb / bs);
     const bool ok = page >= 0 && page < p.num_blocks;
     const uint16_t* base = cache + (static_cast<int64_t>(ok ? page : 0) * bs + (tb % bs)) * D;
     const uint32_t lbase = lds_addr(&ktile[kb][0]);
