@@ -109,13 +109,18 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   constexpr int MPW = MT / NW;              // latent tiles per wave (value product)
   constexpr int NPF = NW * 4;               // P^T fragments per tile: (head tile, k-step)
   constexpr int NPV = NPF * MPW;            // value MFMAs per wave per tile
-  constexpr int VPS = 32 / NPV;             // scores exponentiated per value MFMA
+  // The 32 exponentials of a lane are spread over the first kExpSlots value
+  // MFMAs (slot s handles scores exp_lo(s) .. exp_lo(s+1)-1), so the last
+  // P^T fragment is stored well before the step's barrier.
+  constexpr int kExpSlots = NPV;
+  auto exp_lo = [](int s) constexpr { return s >= kExpSlots ? 32 : (s * 32) / kExpSlots; };
   static_assert(SLOTS % NT == 0, "tile must split evenly over the workgroup");
   static_assert(CPR % 8 == 0 && DS % 64 == 0 && DR % 16 == 0, "shape");
   static_assert(MT % NW == 0 && MPW % 2 == 0, "latent tiles per wave");
   static_assert(((KL / 4) & (KL / 4 - 1)) == 0, "latent k-step groups must be a power of two");
-  static_assert(32 % NPV == 0 && KS > 2 * MPW, "schedule shape");
-  static_assert(2 * IPT <= KS && IPT < 64, "copies per tile must fit the score k-steps");
+  static_assert(NPV <= 32 && kExpSlots <= NPV && KS > 2 * MPW, "schedule shape");
+  static_assert(2 * IPT <= KS && IPT < 32, "copies per tile must fit the score k-steps");
+  static_assert(kMaxTiles % NT == 0, "tile table fill");
 
   constexpr int NB = 3;                     // K buffers
   __shared__ __attribute__((aligned(1024))) uint4 ktile[NB][SLOTS];
@@ -139,7 +144,51 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   const int head0 = hg * (32 * NW);              // first head of the group
   const int head = head0 + wave * 32 + l31;      // this lane's score head
 
+  // ---- k-step order: latent k-steps rotated so this wave's own latent
+  // tiles (k-steps 2*MPW*wave ..) come first, then the rope k-steps ----
+  const int rot4 = (MPW / 2) * wave;             // rotation in groups of 4 k-steps
+  auto phys_ks = [&](int kk) -> int {
+    return kk < KL ? (((kk >> 2) + rot4) & (KL / 4 - 1)) * 4 + (kk & 3) : kk;
+  };
+
+  // The first memory round trip carries everything that does not depend on
+  // the sequence length: the block ids of the split's first two tiles
+  // (index clamped into the table row; unused if the tile does not exist)
+  // and the query fragments (B operand of S^T, in rotated k-step order).
+  const int32_t* bt_row = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
+  const int bs = p.block_size;
+  int pg[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    pg[t] = scalar_load(bt_row + min((split * p.chunk + t * kTile) / bs, p.max_blocks - 1));
+  bf16x8_t qf[KS];
+  {
+    const uint16_t* ql = static_cast<const uint16_t*>(p.q_latent) + b * p.qls_b + head * p.qls_h;
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + b * p.qrs_b + head * p.qrs_h;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int k = phys_ks(kk) * 16 + 8 * half;
+      qf[kk] = *reinterpret_cast<const bf16x8_t*>((k < DS) ? (ql + k) : (qr + (k - DS)));
+    }
+  }
+  // ... and the block ids of every tile the split may cover (one per
+  // thread and pass), for the tile table the steps read.
+  constexpr int kFill = kMaxTiles / NT;
+  const int ctiles = p.chunk / kTile;
+  int fpg[kFill];
+#pragma unroll
+  for (int k = 0; k < kFill; ++k) {
+    const int t = k * NT + static_cast<int>(threadIdx.x);
+    fpg[k] = t < ctiles ? bt_row[min((split * p.chunk + t * kTile) / bs, p.max_blocks - 1)] : 0;
+  }
   int L = scalar_load(p.seq_lens + b);
+  // One wait for all of it, before the branch on L, so the loads above are
+  // issued together instead of after the length check.
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) asm volatile("" : : "v"(qf[kk]));
+#pragma unroll
+  for (int k = 0; k < kFill; ++k) asm volatile("" : : "v"(fpg[k]));
+  asm volatile("" : : "s"(pg[0]), "s"(pg[1]), "s"(L));
   L = max(0, min(L, min(p.max_seq_len, p.max_blocks * p.block_size)));
   const int t0 = split * p.chunk;
   const int t1 = min(L, t0 + p.chunk);
@@ -151,14 +200,6 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;
   const int nfull = (t1 - t0) / kTile;
 
-  // ---- k-step order: latent k-steps rotated so this wave's own latent
-  // tiles (k-steps 2*MPW*wave ..) come first, then the rope k-steps ----
-  const int rot4 = (MPW / 2) * wave;             // rotation in groups of 4 k-steps
-  auto phys_ks = [&](int kk) -> int {
-    return kk < KL ? (((kk >> 2) + rot4) & (KL / 4 - 1)) * 4 + (kk & 3) : kk;
-  };
-
-  bf16x8_t qf[KS];       // query fragments, loaded once the first copies are out
   bf16x8_t ident[2];     // 0/1 B operands of the transposing MFMAs
 
   // ---- tile copies: chunk slot (i*NW + wave)*64 + lane of a tile ----
@@ -172,8 +213,6 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     src_off[i] = static_cast<uint32_t>((r * D + c * 8) * 2);
   }
   const uint16_t* cache = static_cast<const uint16_t*>(p.cache);
-  const int32_t* bt_row = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
-  const int bs = p.block_size;
   // First cache row of tile t, in units of 64 rows; an out-of-range block
   // id reads the cache's first rows (unspecified output, no access outside
   // the cache).
@@ -254,38 +293,43 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[mt][r] = 0.f;
-    f32x16_t tacc[2];
+    // tacc[mm][mt]: transposition of latent tile mm, token rows 32*mt ..
+    f32x16_t tacc[MPW][2];
     bf16x8_t qa[4];
     qa[0] = rd_k(T, 0, 0);
     qa[1] = rd_k(T, 0, 1);
     qa[2] = rd_k(T, 1, 0);
     qa[3] = rd_k(T, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
+    // The fp32 -> bf16 conversion of the transposed tiles is spread over the
+    // later k-steps (one 8-value piece per odd k-step from kCv0 on), so its
+    // register reads run in the shadow of the score MFMAs instead of waiting
+    // for the transposing MFMAs to finish.
+    constexpr int kPieces = MPW * 4;          // (mm, mt, hf)
+    constexpr int kCv0 = KS - 2 * kPieces + 1;
+    static_assert(kCv0 >= 2 * MPW + 1, "conversions must start after the last transposition");
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       sc[0] = mfma(qa[(2 * kk) & 3], qf[kk], sc[0]);
-      if (kk >= 2 && kk <= 2 * MPW && (kk & 1) == 0) {
-        // latent tile (kk - 2) / 2 is transposed: A fragments of the value
-        // product for token k-steps j = 2*mt + hf
-        const int mm = (kk - 2) >> 1;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vt[mm][2 * mt + hf][e] = static_cast<__bf16>(tacc[mt][8 * hf + e]);
-      }
       if (kk < 2 * MPW) {
         const f32x16_t z = {};
-        tacc[0] = mfma(qa[(2 * kk) & 3], ident[kk & 1], (kk & 1) ? tacc[0] : z);
+        tacc[kk >> 1][0] = mfma(qa[(2 * kk) & 3], ident[kk & 1], (kk & 1) ? tacc[kk >> 1][0] : z);
       }
       if (kk + 2 < KS) qa[(2 * kk) & 3] = rd_k(T, kk + 2, 0);
       sc[1] = mfma(qa[(2 * kk + 1) & 3], qf[kk], sc[1]);
       if (kk < 2 * MPW) {
         const f32x16_t z = {};
-        tacc[1] = mfma(qa[(2 * kk + 1) & 3], ident[kk & 1], (kk & 1) ? tacc[1] : z);
+        tacc[kk >> 1][1] = mfma(qa[(2 * kk + 1) & 3], ident[kk & 1], (kk & 1) ? tacc[kk >> 1][1] : z);
       }
       if (kk + 2 < KS) qa[(2 * kk + 1) & 3] = rd_k(T, kk + 2, 1);
+      if (kk >= kCv0 && ((kk - kCv0) & 1) == 0) {
+        // piece (mm, mt, hf): value A fragment for token k-step j = 2*mt + hf
+        const int pc = (kk - kCv0) >> 1;
+        const int mm = pc >> 2, mt = (pc >> 1) & 1, hf = pc & 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vt[mm][2 * mt + hf][e] = static_cast<__bf16>(tacc[mm][mt][8 * hf + e]);
+        asm volatile("" : "+v"(vt[mm][2 * mt + hf]));   // convert here, not at the loop latch
+      }
       if ((kk & 1) == 0 && kk / 2 < IPT && cj != nullptr) copy_chunk(*cj, kk / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -342,9 +386,9 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
 #pragma unroll
       for (int mm = 0; mm < MPW; ++mm) {
         oacc[mm][ht] = mfma(vc[mm][j], pa[f % 3], oacc[mm][ht]);
+        const int slot = f * MPW + mm;
 #pragma unroll
-        for (int e = 0; e < VPS; ++e) {
-          const int v = (f * MPW + mm) * VPS + e;
+        for (int v = exp_lo(slot); v < exp_lo(slot + 1); ++v) {
           float sv = sc[v >> 4][v & 15];
           if (masked) {
             const int row = (v >> 4) * 32 + 8 * ((v & 15) >> 2) + (v & 3);
@@ -406,28 +450,13 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   };
 
   // ---- prologue ----
-  // Tiles 0 and 1 go out first, then the query loads; the compiler's wait
-  // for the query (it cannot see the copies) then also covers tiles 0 and
-  // 1, which the first score product needs anyway.  Tile 2 is issued after
-  // that wait so that it does not hold the first step back.
-  {
-    int pg[3];
+  // The query has arrived (waited for above, before any tile copy was out,
+  // so that wait covered nothing else).  Tiles 0 and 1 go out back to back;
+  // tile 2's copies are spread over the first score product, which waits
+  // for tile 0 only.  (Issuing more at once only holds the wave: every CU
+  // starts at the same time and the copies queue behind each other.)
 #pragma unroll
-    for (int t = 0; t < 3; ++t)
-      pg[t] = t < ntiles ? scalar_load(bt_row + (t0 + t * kTile) / bs) : 0;
-    copy_all(make_job(0, 0, tile_row(0, pg[0])));
-    copy_all(make_job(1, 1, tile_row(1, pg[1])));
-    const uint16_t* ql = static_cast<const uint16_t*>(p.q_latent) + b * p.qls_b + head * p.qls_h;
-    const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + b * p.qrs_b + head * p.qrs_h;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int k = phys_ks(kk) * 16 + 8 * half;   // query fragments in rotated order
-      qf[kk] = *reinterpret_cast<const bf16x8_t*>((k < DS) ? (ql + k) : (qr + (k - DS)));
-    }
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) asm volatile("" : : "v"(qf[kk]));
-    copy_all(make_job(2, 2, tile_row(2, pg[2])));
-  }
+  for (int t = 0; t < 2; ++t) copy_all(make_job(t, t, t < ntiles ? tile_row(t, pg[t]) : 0u));
   // 0/1 B operands: ident[0] picks k = j, ident[1] picks k = j - 16 for
   // output column j (lane l holds column l % 32, k-slots 8*(l/32) ..).
 #pragma unroll
@@ -435,11 +464,11 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     ident[0][e] = static_cast<__bf16>((l31 == 8 * half + e) ? 1.0f : 0.0f);
     ident[1][e] = static_cast<__bf16>((l31 == 16 + 8 * half + e) ? 1.0f : 0.0f);
   }
-  // Table of tile rows for the steps (scalar reads: a vector load's wait
-  // would also wait for tile 2).
-  for (int t = wave; t < min(ntiles, kMaxTiles); t += NW) {
-    const uint32_t r = tile_row(t, scalar_load(bt_row + (t0 + t * kTile) / bs));
-    if (lane == 0) trow[t] = r;
+  // Table of tile rows for the steps.
+#pragma unroll
+  for (int k = 0; k < kFill; ++k) {
+    const int t = k * NT + static_cast<int>(threadIdx.x);
+    if (t < ntiles) trow[t] = tile_row(t, fpg[k]);
   }
 
   bool first = true;
@@ -454,13 +483,14 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     m_seen = -INFINITY;
     if (!first) {
 #pragma unroll
-      for (int t = 0; t < 3; ++t) copy_all(make_job(t, t, __builtin_amdgcn_readfirstlane(trow[min(t, ntiles - 1)])));
-      wait_vm(std::integral_constant<int, IPT>());
+      for (int t = 0; t < 2; ++t) copy_all(make_job(t, t, __builtin_amdgcn_readfirstlane(trow[min(t, ntiles - 1)])));
     }
+    wait_vm(std::integral_constant<int, IPT>());       // tile 0
     barrier();
     {
+      const CopyJob cj2 = make_job(2, 2, __builtin_amdgcn_readfirstlane(trow[min(2, ntiles - 1)]));
       f32x16_t sc[2];
-      scores(reinterpret_cast<const char*>(&ktile[0][0]), sc, vc, nullptr);
+      scores(reinterpret_cast<const char*>(&ktile[0][0]), sc, vc, &cj2);
       if (nfull == 0) {
         const int lim = t1 - t0 - 4 * half;
 #pragma unroll
@@ -481,6 +511,8 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
       }
       put_p(&ptile[0][0], pn);
     }
+    wait_vm(std::integral_constant<int, IPT>());       // tile 1 (step 0's barrier shares it)
+
     for (int i = 0; i + 1 < nfull; ++i) step(i, false);
     if (nfull >= 1 && nfull < ntiles) step(nfull - 1, true);
     wait_copies();   // the trailing re-reads land before any K buffer is reused
