@@ -212,7 +212,7 @@ typedef struct tpla_decode_args {
   int32_t num_splits;          /* token splits per sequence; 0 = automatic.     */
                                /* A request: raised where a kernel caps the     */
                                /* tokens of one split (65536 on the bf16        */
-                               /* streaming kernel for 128-head groups)         */
+                               /* streaming kernel, block_size % 64 == 0)       */
 } tpla_decode_args;
 
 /*

@@ -1,19 +1,23 @@
-// Streaming bf16 matrix-core split-K decode of one TPLA shard, with the
-// value product split over the latent columns (gfx950).
+// Streaming bf16 matrix-core split-K decode of one TPLA shard (gfx950).
 //
-// Same computation as decode_stream.hip (per-shard attention of the absorbed
-// query slice plus the whole rope query over the shard's cached rows, value
-// = the latent slice, the shard's own softmax; TPLA abstract, edgentiq blog
-// "How TPLA Works"), with the work of a workgroup divided differently:
+// Per-shard attention of the absorbed query slice plus the whole rope query
+// over the shard's cached rows [latent slice || rope]; the value is the
+// latent slice; the softmax is the shard's own (TPLA abstract; edgentiq
+// blog, "How TPLA Works: Smart Slicing and Reparameterization").  Needs
+// block_size % 64 == 0, so a 64-token tile is one contiguous run of
+// 64 * (d_s + d_r) * 2 bytes inside one page.
+//
+// One workgroup of NW waves per (token split, sequence, group of 32*NW
+// heads).  Per 64-token tile the work is divided two ways:
 //
 //   scores   wave w owns heads 32w .. 32w+31 of the group:
 //            S^T[token, head] = K_tile . Q^T, then P = exp2(c*S - m_ref)
 //   values   wave w owns latent columns 32*MPW*w .. +32*MPW, for every head
 //            of the group: O^T[lat, head] += V^T . P^T
 //
-// The matrix cores wait on operand loads (about 30 cycles per KiB a wave
-// moves from LDS into registers while MFMAs run), so the point of the split
-// is to move fewer bytes per MFMA:
+// all on v_mfma_f32_32x32x16_bf16.  The matrix cores wait on operand loads
+// (about 30 cycles per KiB a wave moves from LDS into registers while MFMAs
+// run), so the split is about moving few bytes per MFMA:
 // * P^T fragments are exchanged through LDS (each wave writes its 32 heads,
 //   4 KiB per tile) and each fragment feeds MPW value MFMAs.
 // * V^T never goes through LDS.  The value A operand needs 8 consecutive
@@ -27,18 +31,25 @@
 //   own MPW latent tiles; it visits their k-steps first (the k-step order is
 //   rotated per wave, and the query fragments are loaded in that order).
 // * Tiles go from HBM straight into LDS (global_load_lds_dwordx4 from
-//   inline assembly, waited for explicitly) in the swizzled layout of the
-//   other streaming kernel, conflict-free for the score A-fragment reads.
-//   Three K buffers: tile i+3 is copied while tiles i+1 and i+2 are in
-//   use, so a copy has a whole step to land.  The copy instructions are
-//   spread over the score MFMAs: issued back to back they hold the wave
-//   for about as long as the vector memory unit takes to accept them.
+//   inline assembly, waited for explicitly: the compiler would otherwise
+//   wait for every copy in flight before each LDS read).  16-byte chunk c of
+//   tile row r sits at chunk position (c & ~7) | ((c & 7) ^ swz(r)) of the
+//   row, which keeps the score A-fragment reads (16 rows, one chunk, per 16
+//   lanes) free of bank conflicts.  With three K buffers tile i+3 is copied
+//   while tiles i+1 and i+2 are in use (a copy has a whole step to land);
+//   with two, tile i+2 is copied during step i.  The copy instructions ride
+//   on the score MFMAs: issued back to back they hold the wave for about as
+//   long as the vector memory unit takes to accept them.
+// * The block ids of the split's tiles go to an LDS table once; their loads
+//   share the kernel's first memory round trip with the query and the
+//   sequence length.
 // * The P^T fragments are stored as soon as each is complete, and the
 //   cross-half max uses v_permlane32_swap, so no LDS wait ends a step.
 // * Softmax against a fixed reference max (the split's first tile max); a
 //   later tile max more than 64 (base 2) above it makes the split run again
 //   with the raised reference.  Accumulators are touched only by MFMAs.
-// * Work units are spread so that the splits of a sequence share an XCD.
+// * Work units are spread so that the splits of a sequence share an XCD
+//   (workgroup n runs on XCD n % 8).
 #include <type_traits>
 
 #include "tpla_internal.h"
@@ -94,7 +105,7 @@ __device__ __forceinline__ f32x16_t mfma(const bf16x8_t& a, const bf16x8_t& b, c
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int NW, int DS, int DR>
+template <int NW, int DS, int DR, int NB>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(1, 1)))
 void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
@@ -119,10 +130,18 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   static_assert(MT % NW == 0 && MPW % 2 == 0, "latent tiles per wave");
   static_assert(((KL / 4) & (KL / 4 - 1)) == 0, "latent k-step groups must be a power of two");
   static_assert(NPV <= 32 && kExpSlots <= NPV && KS > 2 * MPW, "schedule shape");
-  static_assert(2 * IPT <= KS && IPT < 32, "copies per tile must fit the score k-steps");
+  // Tile copies: the first kCopyS ride on the score k-steps (one every
+  // kCopyEveryS), any rest on the value MFMAs (one every kCopyEveryV).
+  // Measured on the DeepSeek-V3 shard: all ten on the score k-steps is ~1-2%
+  // faster than half and half.
+  constexpr int kCopyS = IPT;
+  constexpr int kCopyEveryS = KS / kCopyS;
+  constexpr int kCopyEveryV = (IPT - kCopyS) > 0 ? NPF / (IPT - kCopyS) : NPF;
+  static_assert(kCopyS * kCopyEveryS <= KS && (IPT - kCopyS) * kCopyEveryV <= NPF && IPT < 32,
+                "copies per tile must fit the step");
   static_assert(kMaxTiles % NT == 0, "tile table fill");
 
-  constexpr int NB = 3;                     // K buffers
+  static_assert(NB == 2 || NB == 3, "K buffers");
   __shared__ __attribute__((aligned(1024))) uint4 ktile[NB][SLOTS];
   __shared__ __attribute__((aligned(1024))) uint4 ptile[2][NPF * 64];
   __shared__ uint32_t trow[kMaxTiles];   // first cache row of each tile / 64
@@ -302,12 +321,18 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     qa[3] = rd_k(T, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     // The fp32 -> bf16 conversion of the transposed tiles is spread over the
-    // later k-steps (one 8-value piece per odd k-step from kCv0 on), so its
-    // register reads run in the shadow of the score MFMAs instead of waiting
-    // for the transposing MFMAs to finish.
+    // later k-steps (one 8-value piece every other k-step from kCv0 on, or
+    // kPer pieces per k-step when there are few k-steps), so its register
+    // reads run in the shadow of the score MFMAs instead of waiting for the
+    // transposing MFMAs to finish.
     constexpr int kPieces = MPW * 4;          // (mm, mt, hf)
-    constexpr int kCv0 = KS - 2 * kPieces + 1;
-    static_assert(kCv0 >= 2 * MPW + 1, "conversions must start after the last transposition");
+    constexpr int kStart = 2 * MPW + 1;       // one k-step after the last transposition
+    constexpr bool kSparse = KS - kStart >= 2 * kPieces - 1;
+    constexpr int kCv0 = kSparse ? KS - 2 * kPieces + 1 : kStart;
+    constexpr int kStride = kSparse ? 2 : 1;
+    constexpr int kPer = kSparse ? 1 : (kPieces + (KS - kStart) - 1) / (KS - kStart);
+    static_assert(kCv0 >= kStart && kCv0 + ((kPieces + kPer - 1) / kPer - 1) * kStride < KS,
+                  "conversions must fit after the last transposition");
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       sc[0] = mfma(qa[(2 * kk) & 3], qf[kk], sc[0]);
@@ -322,15 +347,21 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
         tacc[kk >> 1][1] = mfma(qa[(2 * kk + 1) & 3], ident[kk & 1], (kk & 1) ? tacc[kk >> 1][1] : z);
       }
       if (kk + 2 < KS) qa[(2 * kk + 1) & 3] = rd_k(T, kk + 2, 1);
-      if (kk >= kCv0 && ((kk - kCv0) & 1) == 0) {
-        // piece (mm, mt, hf): value A fragment for token k-step j = 2*mt + hf
-        const int pc = (kk - kCv0) >> 1;
-        const int mm = pc >> 2, mt = (pc >> 1) & 1, hf = pc & 1;
+      if (kk >= kCv0 && (kk - kCv0) % kStride == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vt[mm][2 * mt + hf][e] = static_cast<__bf16>(tacc[mm][mt][8 * hf + e]);
-        asm volatile("" : "+v"(vt[mm][2 * mt + hf]));   // convert here, not at the loop latch
+        for (int q = 0; q < kPer; ++q) {
+          // piece (mm, mt, hf): value A fragment for token k-step j = 2*mt + hf
+          const int pc = ((kk - kCv0) / kStride) * kPer + q;
+          if (pc < kPieces) {
+            const int mm = pc >> 2, mt = (pc >> 1) & 1, hf = pc & 1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vt[mm][2 * mt + hf][e] = static_cast<__bf16>(tacc[mm][mt][8 * hf + e]);
+            asm volatile("" : "+v"(vt[mm][2 * mt + hf]));   // convert here, not at the loop latch
+          }
+        }
       }
-      if ((kk & 1) == 0 && kk / 2 < IPT && cj != nullptr) copy_chunk(*cj, kk / 2);
+      if (cj != nullptr && kk % kCopyEveryS == 0 && kk / kCopyEveryS < kCopyS)
+        copy_chunk(*cj, kk / kCopyEveryS);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -368,7 +399,7 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   // with the exponentials of the next tile's scores sc interleaved (masked
   // rows >= lim get P = 0); the new P^T goes to pn.
   auto values = [&](int pb, const f32x16_t (&sc)[2], int lim, bool masked, uint4* pdst,
-                    float& mx) {
+                    float& mx, const CopyJob& cj) {
     const uint4* P = &ptile[pb][0];
     bf16x8_t pn[4];
     auto frag = [&](int f) -> bf16x8_t {
@@ -402,6 +433,7 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
         }
       }
       if (f + 3 < NPF) pa[f % 3] = frag(f + 3);
+      if (f % kCopyEveryV == 1 && kCopyS + f / kCopyEveryV < IPT) copy_chunk(cj, kCopyS + f / kCopyEveryV);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -430,8 +462,8 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   auto step = [&](int i, bool masked) {
     // The tile table read waits for this wave's LDS traffic, as the
     // barrier does anyway.
-    const uint32_t row64 = __builtin_amdgcn_readfirstlane(trow[min(i + 3, ntiles - 1)]);
-    const CopyJob cj = make_job(i + 3, i % NB, row64);
+    const uint32_t row64 = __builtin_amdgcn_readfirstlane(trow[min(i + NB, ntiles - 1)]);
+    const CopyJob cj = make_job(i + NB, i % NB, row64);
     barrier();
     const char* T = reinterpret_cast<const char*>(&ktile[(i + 1) % NB][0]);
     f32x16_t sc[2];
@@ -439,14 +471,16 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     scores(T, sc, vn, &cj);
     const int lim = t1 - (t0 + (i + 1) * kTile) - 4 * half;
     float mx = -INFINITY;
-    values(i & 1, sc, lim, masked, &ptile[(i + 1) & 1][0], mx);
+    values(i & 1, sc, lim, masked, &ptile[(i + 1) & 1][0], mx, cj);
 #pragma unroll
     for (int m = 0; m < MPW; ++m)
 #pragma unroll
       for (int j = 0; j < 4; ++j) vc[m][j] = vn[m][j];
     mx = both_halves_max(mx) * c;
     if (mx > m_run + kRescale) m_seen = fmaxf(m_seen, mx);
-    wait_vm(std::integral_constant<int, IPT>());
+    // NB == 3: tile i+2 (copied during step i-1) must be in; NB == 2: tile
+    // i+2, copied during this step.
+    wait_vm(std::integral_constant<int, NB == 3 ? IPT : 0>());
   };
 
   // ---- prologue ----
@@ -488,9 +522,15 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     wait_vm(std::integral_constant<int, IPT>());       // tile 0
     barrier();
     {
-      const CopyJob cj2 = make_job(2, 2, __builtin_amdgcn_readfirstlane(trow[min(2, ntiles - 1)]));
       f32x16_t sc[2];
-      scores(reinterpret_cast<const char*>(&ktile[0][0]), sc, vc, &cj2);
+      if constexpr (NB == 3) {
+        const CopyJob cj2 = make_job(2, 2, __builtin_amdgcn_readfirstlane(trow[min(2, ntiles - 1)]));
+        scores(reinterpret_cast<const char*>(&ktile[0][0]), sc, vc, &cj2);
+#pragma unroll
+        for (int ci = kCopyS; ci < IPT; ++ci) copy_chunk(cj2, ci);
+      } else {
+        scores(reinterpret_cast<const char*>(&ktile[0][0]), sc, vc, nullptr);
+      }
       if (nfull == 0) {
         const int lim = t1 - t0 - 4 * half;
 #pragma unroll
@@ -511,7 +551,7 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
       }
       put_p(&ptile[0][0], pn);
     }
-    wait_vm(std::integral_constant<int, IPT>());       // tile 1 (step 0's barrier shares it)
+    wait_vm(std::integral_constant<int, NB == 3 ? IPT : 0>());   // tile 1 (step 0's barrier shares it)
 
     for (int i = 0; i + 1 < nfull; ++i) step(i, false);
     if (nfull >= 1 && nfull < ntiles) step(nfull - 1, true);
@@ -578,13 +618,13 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   }
 }
 
-template <int NW, int DS, int DR>
+template <int NW, int DS, int DR, int NB>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
   if (p.chunk > kMaxTiles * kTile) return hipErrorInvalidValue;
   const int HG = p.heads / (32 * NW);
   const int n_units = p.num_splits * p.batch * HG;
   const int per_xcd = (n_units + 7) / 8;
-  hipLaunchKernelGGL((decode_latsplit_kernel<NW, DS, DR>), dim3(8 * per_xcd), dim3(NW * 64), 0, s,
+  hipLaunchKernelGGL((decode_latsplit_kernel<NW, DS, DR, NB>), dim3(8 * per_xcd), dim3(NW * 64), 0, s,
                      p, n_units, per_xcd);
   return hipGetLastError();
 }
@@ -595,13 +635,21 @@ int decode_latsplit_max_chunk() { return kMaxTiles * kTile; }
 
 int decode_latsplit_partial_block() { return 64; }
 
+// Instantiations: 128-head groups with d_s = 256 (four waves, three K
+// buffers, one workgroup per CU) and 64-head groups with d_s = 128 (two
+// waves, two K buffers, two workgroups per CU); both with d_r = 64.
 bool decode_latsplit_supported(int heads, int d_s, int d_r, int block_size) {
-  return block_size % kTile == 0 && heads % 128 == 0 && d_s == 256 && d_r == 64;
+  if (block_size % kTile != 0 || d_r != 64) return false;
+  if (heads % 128 == 0 && d_s == 256) return true;
+  return heads % 64 == 0 && d_s == 128;
 }
 
+int decode_latsplit_groups_per_cu(int heads, int d_s) { return (heads % 128 == 0 && d_s == 256) ? 1 : 2; }
+
 hipError_t launch_decode_latsplit(const DecodeParams& p, hipStream_t s) {
-  if (decode_latsplit_supported(p.heads, p.d_s, p.d_r, p.block_size)) return launch_t<4, 256, 64>(p, s);
-  return hipErrorNotSupported;
+  if (!decode_latsplit_supported(p.heads, p.d_s, p.d_r, p.block_size)) return hipErrorNotSupported;
+  if (p.heads % 128 == 0 && p.d_s == 256) return launch_t<4, 256, 64, 3>(p, s);
+  return launch_t<2, 128, 64, 2>(p, s);
 }
 
 }  // namespace tpla

@@ -82,7 +82,7 @@ bool mfma_operands_ok(const tpla_decode_args* a) {
 
 Path decode_path(const tpla_decode_args* a) {
   if (!mfma_operands_ok(a)) return Path::kGeneric;
-  if (tpla::decode_stream_supported(a->heads, a->d_s, a->d_r, a->block_size)) return Path::kStream;
+  if (tpla::decode_latsplit_supported(a->heads, a->d_s, a->d_r, a->block_size)) return Path::kStream;
   if (tpla::decode_mfma_supported(a->heads, a->d_s, a->d_r)) return Path::kMfma;
   return Path::kGeneric;
 }
@@ -140,7 +140,7 @@ tpla_status plan_decode(const tpla_decode_args* a, Plan* pl) {
     if (path != Path::kGeneric) {
       groups *= a->heads / (32 * (a->heads % 128 == 0 ? 4 : (a->heads % 64 == 0 ? 2 : 1)));
       per_cu = path == Path::kStream
-                   ? tpla::decode_stream_groups_per_cu(a->heads, a->d_s, a->d_r)
+                   ? tpla::decode_latsplit_groups_per_cu(a->heads, a->d_s)
                    : tpla::decode_mfma_groups_per_cu(a->heads, a->d_s, a->d_r);
     } else {
       groups *= (a->heads + 7) / 8;
@@ -352,7 +352,7 @@ tpla_status tpla_decode_shard(const tpla_decode_args* a, void* workspace, size_t
 
   hipError_t e;
   switch (decode_path(a)) {
-    case Path::kStream: e = tpla::launch_decode_stream(p, s); break;
+    case Path::kStream: e = tpla::launch_decode_latsplit(p, s); break;
     case Path::kMfma: e = tpla::launch_decode_mfma(p, s); break;
     default: e = tpla::launch_decode_generic(p, a->dtype == TPLA_BF16, s); break;
   }
