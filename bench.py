@@ -220,13 +220,16 @@ def main():
     combined = torch.empty((B, H, len(shards) * d_s), dtype=torch.float32, device="cuda")
     args0 = tpla.make_decode_args(q_rot[:, :, :d_s], q_rope, caches[0][0], bt, lens, cfg.scale,
                                   maxlen, outs[0], lses[0], args.num_splits)
+    # split count from the host's copy of the lengths (a serving loop has them)
+    splits = args.num_splits or tpla.decode_suggest_splits(args0, case.seq_lens)
+    args0.num_splits = splits
     ws_bytes = tpla.decode_workspace_size(args0)
     workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
     def decode(r, i, g):
         tpla.decode_shard(q_rot[:, :, g * d_s:(g + 1) * d_s], q_rope, caches[r][i], bt, lens,
-                          cfg.scale, maxlen, out=outs[i], lse=lses[i], num_splits=args.num_splits,
+                          cfg.scale, maxlen, out=outs[i], lse=lses[i], num_splits=splits,
                           workspace=workspace)
 
     def step(r):
@@ -329,7 +332,7 @@ def main():
                    "shards_run": len(shards), "d_s": d_s, "d_r": d_r,
                    "context": (list(cfg.ctx) if isinstance(cfg.ctx, tuple) else cfg.ctx),
                    "tokens_attended": lens_sum, "block_size": cfg.block_size,
-                   "cache_replicas": replicas, "global_batch": B,
+                   "cache_replicas": replicas, "global_batch": B, "num_splits": splits,
                    "seq_len": maxlen},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),

@@ -224,6 +224,23 @@ typedef struct tpla_decode_args {
 tpla_status tpla_decode_workspace_size(const tpla_decode_args* args, size_t* bytes);
 
 /*
+ * tpla_decode_suggest_splits: a value for args->num_splits chosen from the
+ * host's copy of the sequence lengths (seq_lens_host[b], b < batch: the
+ * same lengths the device array holds).  The automatic split count sees
+ * only max_seq_len, which for a ragged batch leaves many splits empty and a
+ * few long ones; this one models a launch of the streaming kernel (work
+ * units in launch order, their XCD, one or two workgroups per CU, a fixed
+ * start and finish per unit) and returns the count with the shortest
+ * modelled launch, preferring fewer splits on ties.  For shapes that do not
+ * run the streaming kernel it returns the automatic count.  It reads
+ * nothing on the device and launches nothing; args->num_splits is ignored.
+ * Errors: as tpla_decode_workspace_size; TPLA_ERR_NULL for a NULL
+ * seq_lens_host or num_splits.
+ */
+tpla_status tpla_decode_suggest_splits(const tpla_decode_args* args, const int32_t* seq_lens_host,
+                                       int32_t* num_splits);
+
+/*
  * tpla_decode_shard: one device's share of a TPLA decode step.
  *
  * Per-shard attention with the shard's own softmax (abstract: attention is

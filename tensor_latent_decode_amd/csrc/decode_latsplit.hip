@@ -646,6 +646,8 @@ bool decode_latsplit_supported(int heads, int d_s, int d_r, int block_size) {
 
 int decode_latsplit_groups_per_cu(int heads, int d_s) { return (heads % 128 == 0 && d_s == 256) ? 1 : 2; }
 
+int decode_latsplit_heads_per_group(int heads, int d_s) { return (heads % 128 == 0 && d_s == 256) ? 128 : 64; }
+
 hipError_t launch_decode_latsplit(const DecodeParams& p, hipStream_t s) {
   if (!decode_latsplit_supported(p.heads, p.d_s, p.d_r, p.block_size)) return hipErrorNotSupported;
   if (p.heads % 128 == 0 && p.d_s == 256) return launch_t<4, 256, 64, 3>(p, s);

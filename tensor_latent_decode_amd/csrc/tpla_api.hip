@@ -2,11 +2,13 @@
 // kernel dispatch.  Nothing here allocates device memory or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "tpla.h"
 #include "tpla_internal.h"
@@ -165,9 +167,77 @@ tpla_status plan_decode(const tpla_decode_args* a, Plan* pl) {
   return TPLA_OK;
 }
 
+// Cost of one streaming-kernel launch with `splits` splits of `chunk`
+// tokens, in tile units: units in the kernel's order (split fastest, then
+// head group, then sequence), unit u on XCD u / per_xcd as the kernel maps
+// them, in-order list scheduling onto the XCD's CU slots; a non-empty unit
+// costs its tiles plus a fixed start and finish, an empty one nearly
+// nothing.  Used only to pick a split count from host-side lengths.
+double stream_launch_cost(const int32_t* lens, int batch, int hg, int max_len, int splits, int chunk,
+                          int cus, int per_cu) {
+  constexpr double kFixed = 6.0;     // start-up + tail, in tile steps
+  const int64_t n_units = static_cast<int64_t>(splits) * batch * hg;
+  const int64_t per_xcd = (n_units + 7) / 8;
+  const int slots = std::max(1, cus / 8) * per_cu;
+  double worst = 0.0;
+  std::vector<double> load(static_cast<size_t>(slots));
+  for (int x = 0; x < 8; ++x) {
+    std::fill(load.begin(), load.end(), 0.0);
+    for (int64_t u = x * per_xcd; u < std::min<int64_t>((x + 1) * per_xcd, n_units); ++u) {
+      const int split = static_cast<int>(u % splits);
+      const int b = static_cast<int>(u / splits / hg);
+      const int L = std::max(0, std::min(lens[b], max_len));
+      const int t = std::max(0, std::min(L, (split + 1) * chunk) - split * chunk);
+      const double c = t > 0 ? (t + 63) / 64 + kFixed : 0.02;
+      auto it = std::min_element(load.begin(), load.end());
+      *it += c;
+    }
+    worst = std::max(worst, *std::max_element(load.begin(), load.end()));
+  }
+  return worst;
+}
+
 }  // namespace
 
 extern "C" {
+
+tpla_status tpla_decode_suggest_splits(const tpla_decode_args* args, const int32_t* seq_lens_host,
+                                       int32_t* num_splits) {
+  if (num_splits == nullptr || seq_lens_host == nullptr)
+    return fail(TPLA_ERR_NULL, "seq_lens_host and num_splits are required");
+  tpla_status st = check_decode(args);
+  if (st != TPLA_OK) return st;
+  tpla_decode_args a = *args;
+  a.num_splits = 0;
+  Plan pl;
+  st = plan_decode(&a, &pl);
+  if (st != TPLA_OK) return st;
+  if (decode_path(&a) != Path::kStream) {
+    *num_splits = pl.splits;
+    return ok();
+  }
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != TPLA_OK) return st;
+  const int hg = a.heads / tpla::decode_latsplit_heads_per_group(a.heads, a.d_s);
+  const int per_cu = tpla::decode_latsplit_groups_per_cu(a.heads, a.d_s);
+  const int max_tiles = std::max(1, (a.max_seq_len + 63) / 64);
+  const int cap_tiles = tpla::decode_latsplit_max_chunk() / 64;   // the kernel's tile table
+  int best = pl.splits;
+  double best_cost = 1e300;
+  for (int tiles_per = 1; tiles_per <= std::min(max_tiles, cap_tiles); ++tiles_per) {
+    const int splits = (max_tiles + tiles_per - 1) / tiles_per;
+    if (tiles_per > 1 && (max_tiles + tiles_per - 2) / (tiles_per - 1) == splits) continue;  // same split count
+    const double c = stream_launch_cost(seq_lens_host, a.batch, hg, a.max_seq_len, splits,
+                                        tiles_per * 64, cus, per_cu);
+    if (c < best_cost - 1e-9 || (c < best_cost + 1e-9 && splits < best)) {
+      best_cost = c;
+      best = splits;
+    }
+  }
+  *num_splits = best;
+  return ok();
+}
 
 const char* tpla_status_string(tpla_status s) {
   switch (s) {

@@ -124,6 +124,7 @@ int decode_mfma_groups_per_cu(int heads, int d_s, int d_r);
 hipError_t launch_decode_latsplit(const DecodeParams& p, hipStream_t s);
 bool decode_latsplit_supported(int heads, int d_s, int d_r, int block_size);
 int decode_latsplit_groups_per_cu(int heads, int d_s);   // workgroups per CU the split plan targets
+int decode_latsplit_heads_per_group(int heads, int d_s);
 int decode_latsplit_max_chunk();   // tokens per split the latent-split kernel accepts
 int decode_latsplit_partial_block();   // columns per scale of its fp16 split outputs
 hipError_t launch_decode_generic(const DecodeParams& p, int is_bf16, hipStream_t s);

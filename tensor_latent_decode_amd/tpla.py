@@ -91,8 +91,10 @@ def lib() -> ctypes.CDLL:
     L.tpla_decode_shard.argtypes = [ctypes.POINTER(DecodeArgs), vp, sz, vp]
     L.tpla_combine_shards.argtypes = [ctypes.POINTER(vp), dt, i32, i32, i32, i32, vp, dt, i32, vp]
     L.tpla_rotate_append.argtypes = [ctypes.POINTER(RotateAppendArgs), vp]
+    L.tpla_decode_suggest_splits.argtypes = [ctypes.POINTER(DecodeArgs), vp, ctypes.POINTER(i32)]
     for f in ("tpla_hadamard_latent", "tpla_append_kv", "tpla_decode_workspace_size",
-              "tpla_decode_shard", "tpla_combine_shards", "tpla_rotate_append"):
+              "tpla_decode_shard", "tpla_combine_shards", "tpla_rotate_append",
+              "tpla_decode_suggest_splits"):
         getattr(L, f).restype = ctypes.c_int
     L.tpla_status_string.argtypes = [ctypes.c_int]
     L.tpla_status_string.restype = ctypes.c_char_p
@@ -317,6 +319,19 @@ def make_decode_args(q_latent: torch.Tensor, q_rope: Optional[torch.Tensor], cac
     a.lse = None if lse is None else lse.data_ptr()
     a.num_splits = int(num_splits)
     return a
+
+
+def decode_suggest_splits(args: "DecodeArgs", seq_lens_host) -> int:
+    """Split count for `args` from the host copy of the sequence lengths."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    if lens.shape != (args.batch,):
+        raise ValueError("seq_lens_host must hold one length per sequence")
+    out = ctypes.c_int32(0)
+    _check("tpla_decode_suggest_splits",
+           lib().tpla_decode_suggest_splits(ctypes.byref(args), lens.ctypes.data_as(ctypes.c_void_p),
+                                            ctypes.byref(out)))
+    return int(out.value)
 
 
 def decode_workspace_size(args: DecodeArgs) -> int:

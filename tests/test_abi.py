@@ -18,7 +18,8 @@ def test_exports_every_declared_function():
     names = tpla.header_functions()
     assert {"tpla_hadamard_latent", "tpla_append_kv", "tpla_decode_workspace_size",
             "tpla_decode_shard", "tpla_combine_shards", "tpla_status_string",
-            "tpla_last_error", "tpla_version", "tpla_rotate_append"} <= set(names)
+            "tpla_last_error", "tpla_version", "tpla_rotate_append",
+            "tpla_decode_suggest_splits"} <= set(names)
     raw = ctypes.CDLL(tpla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -186,3 +187,15 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         tpla.hadamard_latent(torch.zeros(4, 16))
+
+
+def test_suggest_splits_argument_checks():
+    L = tpla.lib()
+    a = _args()
+    out = ctypes.c_int32(0)
+    lens = (ctypes.c_int32 * 2)(100, 200)
+    _fails(L.tpla_decode_suggest_splits(ctypes.byref(a), None, ctypes.byref(out)), 1)
+    _fails(L.tpla_decode_suggest_splits(ctypes.byref(a), ctypes.cast(lens, ctypes.c_void_p), None), 1)
+    a.d_s = 0
+    _fails(L.tpla_decode_suggest_splits(ctypes.byref(a), ctypes.cast(lens, ctypes.c_void_p),
+                                        ctypes.byref(out)), 2)

@@ -340,6 +340,41 @@ def test_decode_bf16_late_score_spike(shape, bs):
             assert rel_err(got[b, h], ref[h]) <= TOL_BF16, (b, h)
 
 
+def test_suggested_splits_uniform_and_ragged():
+    """The host-side split suggestion keeps the automatic count for uniform
+    32K lengths (DeepSeek-V3 and Kimi-K2 shards), and a ragged batch decoded
+    with its suggestion matches the oracle."""
+    for heads, d_s in ((128, 256), (64, 128)):
+        a = tpla.DecodeArgs()          # sizes only: the call reads no device memory
+        a.batch, a.heads, a.d_s, a.d_r = 16, heads, d_s, 64
+        a.block_size, a.num_blocks, a.max_blocks_per_seq, a.max_seq_len = 64, 8193, 512, 32768
+        a.dtype, a.scale, a.out_dtype = 1, 0.07, 0
+        fake = 0x10000
+        a.q_latent, a.q_latent_stride_b, a.q_latent_stride_h = fake, heads * 512, 512
+        a.q_rope, a.q_rope_stride_b, a.q_rope_stride_h = fake, heads * 64, 64
+        a.cache, a.block_table, a.seq_lens = fake, fake, fake
+        a.out, a.out_stride_b, a.out_stride_h = fake, heads * d_s, d_s
+        auto = tpla.decode_workspace_size(a)
+        a.num_splits = tpla.decode_suggest_splits(a, np.full(16, 32768, np.int32))
+        assert tpla.decode_workspace_size(a) == auto, (heads, a.num_splits)
+    case = make_case(CONFIGS["ragged_tp2"], batch=8, ctx=(64, 6000), seed=33)
+    gc = GpuCase(case)
+    d_s = case.cfg.d_s
+    cache = gc.prefill(0, d_s)
+    maxlen = int(case.seq_lens.max())
+    out = torch.empty((case.cfg.batch, case.cfg.heads, d_s), dtype=torch.float32, device="cuda")
+    args = tpla.make_decode_args(gc.q_latent[:, :, :d_s], gc.q_rope, cache, gc.bt, gc.hist_lens,
+                                 case.cfg.scale, maxlen, out)
+    sugg = tpla.decode_suggest_splits(args, case.seq_lens - 1)
+    assert 1 <= sugg <= (maxlen + 63) // 64
+    o, _ = tpla.decode_shard(gc.q_latent[:, :, :d_s], gc.q_rope, cache, gc.bt, gc.hist_lens,
+                             case.cfg.scale, maxlen, num_splits=sugg)
+    torch.cuda.synchronize()
+    for b in range(case.cfg.batch):
+        _, parts = oracle_step(case, b, 2, hadamard=False, with_new=False, q_is_rotated=True)
+        assert rel_err(host_f64(o)[b], parts[0][0]) <= TOL_BF16, b
+
+
 @pytest.mark.parametrize("lens", [[1, 2, 63, 64], [65, 127, 128, 129], [4096, 1, 1000, 3]])
 def test_decode_bf16_edge_lengths(lens):
     cases = [make_case(CONFIGS["dsv3_4k"], batch=1, ctx=L, seed=41 + i)
