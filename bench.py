@@ -8,7 +8,8 @@ resident in HBM: rotate the absorbed query and the new token's latent and
 append the new row to the shard caches (tpla_rotate_append: one launch for
 what tpla_hadamard_latent and tpla_append_kv do separately), decode the shard
 (tpla_decode_shard: split-K attention and log-sum-exp merge) and combine the
-shard outputs (tpla_combine_shards).
+shard outputs: every shard's merge writes its latent columns of the combined
+output (the placement tpla_combine_shards performs for outputs held apart).
 The default workload is the DeepSeek-V3-shaped shard at 32K context
 (B=16, H=128, d_c=512 split TP=2 -> d_s=256, d_r=64, paged blocks of 64 with
 a permuted block table); `--workload ragged_tp2` runs both shards of the
@@ -215,9 +216,12 @@ def main():
     del hist_lat, hist_rope, hist_seq, hist_pos
     maxlen = int(case.seq_lens.max())
     q_rot = torch.empty((B, H, d_c), dtype=torch.bfloat16, device="cuda")
-    outs = [torch.empty((B, H, d_s), dtype=torch.float32, device="cuda") for _ in shards]
-    lses = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in shards]
+    # the combine: shard i's merge writes its latent columns of the combined
+    # output directly (placement of disjoint slices; tpla_combine_shards does
+    # the same for outputs held in separate buffers)
     combined = torch.empty((B, H, len(shards) * d_s), dtype=torch.float32, device="cuda")
+    outs = [combined[:, :, i * d_s:(i + 1) * d_s] for i in range(len(shards))]
+    lses = [torch.empty((B, H), dtype=torch.float32, device="cuda") for _ in shards]
     args0 = tpla.make_decode_args(q_rot[:, :, :d_s], q_rope, caches[0][0], bt, lens, cfg.scale,
                                   maxlen, outs[0], lses[0], args.num_splits)
     # split count from the host's copy of the lengths (a serving loop has them)
@@ -237,7 +241,6 @@ def main():
                            first_shard=shards[0])
         for i, g in enumerate(shards):
             decode(r, i, g)
-        tpla.combine_shards(outs, out=combined)
 
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
