@@ -432,6 +432,47 @@ def test_decode_bf16_output_and_determinism():
 # The workloads at their real sizes (sampled sequences)
 # --------------------------------------------------------------------------
 
+@pytest.mark.parametrize("heads,d_c,tp", [(128, 512, 2), (64, 512, 4)])
+def test_decode_split_longer_than_tile_table(heads, d_c, tp):
+    """A single requested split longer than the streaming kernel's tile
+    table (65536 tokens) is planned as more splits and stays exact."""
+    from dataclasses import replace
+    cfg = replace(CONFIGS["dsv3_4k"], heads=heads, d_c=d_c, tp=tp)
+    case = make_case(cfg, batch=1, ctx=70001, seed=72)
+    gc = GpuCase(case)
+    d_s = cfg.d_s
+    cache = gc.prefill(0, d_s)
+    o, _ = tpla.decode_shard(gc.q_latent[:, :, :d_s], gc.q_rope, cache, gc.bt, gc.hist_lens,
+                             cfg.scale, int(case.seq_lens.max()), num_splits=1)
+    torch.cuda.synchronize()
+    _, parts = oracle_step(case, 0, tp, hadamard=False, with_new=False, q_is_rotated=True)
+    assert rel_err(host_f64(o)[0], parts[0][0]) <= TOL_BF16
+
+
+def test_decode_into_combined_columns_equals_combine():
+    """Each shard's decode writing its latent columns of the combined output
+    (strided out) gives the bits tpla_combine_shards gives from separate
+    outputs."""
+    case = make_case(CONFIGS["dsv3_4k"], batch=3, ctx=(100, 900), seed=71)
+    gc = GpuCase(case)
+    cfg = case.cfg
+    d_s = cfg.d_s
+    q = tpla.hadamard_latent(gc.q_latent)
+    maxlen = int(case.seq_lens.max())
+    combined = torch.empty((cfg.batch, cfg.heads, cfg.tp * d_s), dtype=torch.float32, device="cuda")
+    outs = []
+    for g in range(cfg.tp):
+        cache = gc.prefill(g, d_s)
+        o, _ = tpla.decode_shard(q[:, :, g * d_s:(g + 1) * d_s], gc.q_rope, cache, gc.bt,
+                                 gc.hist_lens, cfg.scale, maxlen)
+        tpla.decode_shard(q[:, :, g * d_s:(g + 1) * d_s], gc.q_rope, cache, gc.bt, gc.hist_lens,
+                          cfg.scale, maxlen, out=combined[:, :, g * d_s:(g + 1) * d_s])
+        outs.append(o)
+    ref = tpla.combine_shards(outs)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(combined).view(np.uint32), host_bits(ref).view(np.uint32))
+
+
 def test_dsv3_4k_full():
     case = make_case(CONFIGS["dsv3_4k"])
     gc = GpuCase(case)
