@@ -92,6 +92,7 @@ struct RotateAppendParams {
   int64_t qos;
   int64_t q_rows;
   int q_bf16, q_out_bf16;
+  int q_vec;                    // rows move in 16-byte pieces (set by the launcher)
   const void* lat;              // new latent rows, n wide, unrotated
   int64_t ls;
   const void* rope;             // same dtype as lat
@@ -99,6 +100,7 @@ struct RotateAppendParams {
   void* lat_out;                // optional rotated copy (lat's dtype)
   int64_t los;
   int lat_bf16;
+  int lat_vec;                  // as q_vec, for lat and lat_out
   int n_rows;
   const int32_t* row_seq;
   const int32_t* row_pos;

@@ -61,6 +61,25 @@ def test_hadamard_inplace_strided_rows_and_self_inverse():
     assert rel_err(host_f64(view), host_f64(x.reshape(35, 512))) <= 1e-5
 
 
+@pytest.mark.parametrize("n", [16, 64, 512, 4096])
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_hadamard_unaligned_rows_match_aligned(n, dt):
+    # rows that start one element off a 16-byte boundary take the element-wise
+    # path; its results equal the vector path's bit for bit
+    rng = np.random.default_rng(n + 7)
+    x = torch.from_numpy(rng.standard_normal((23, n)).astype(np.float32)).cuda().to(dt)
+    big = torch.zeros((23, n + 1), dtype=dt, device="cuda")
+    big[:, 1:] = x
+    odd = big[:, 1:]                         # odd row stride, odd start
+    y_al = tpla.hadamard_latent(x)
+    y_odd = torch.empty((23, n + 1), dtype=dt, device="cuda")[:, 1:]
+    tpla.hadamard_latent(odd, out=y_odd)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(y_odd.contiguous()), _bits(y_al))
+    tol = TOL_BF16 if dt == torch.bfloat16 else TOL_FP32
+    assert rel_err(host_f64(y_al), oracle.fwht(host_f64(x))) <= tol
+
+
 # --------------------------------------------------------------------------
 # Paged append (bit-exact)
 # --------------------------------------------------------------------------
@@ -173,6 +192,33 @@ def test_rotate_append_matches_separate_calls(cfg, bs, first, count):
             assert rel_err(row[:d_s], new64[b, g * d_s:(g + 1) * d_s]) <= tol
             want = case.new_rope[b] if case.cfg.dtype == "bf16" else case.new_rope[b].view(np.uint32)
             assert np.array_equal(_bits(c)[int(case.block_table[b, p // bs]), p % bs, d_s:], want)
+
+
+def test_rotate_append_unaligned_rows_match_aligned():
+    # query and new-latent rows off a 16-byte boundary (element-wise path)
+    case = make_case(CONFIGS["dsv3_4k"], batch=3, ctx=(30, 200), seed=23, heads=32)
+    gc = GpuCase(case)
+    n = case.cfg.d_c
+    q = gc.q_latent.reshape(-1, n)
+    qbig = torch.zeros((q.shape[0], n + 1), dtype=q.dtype, device="cuda")
+    qbig[:, 1:] = q
+    nbig = torch.zeros((3, n + 1), dtype=q.dtype, device="cuda")
+    nbig[:, 1:] = gc.new_latent
+    q_out = torch.empty((q.shape[0], n + 1), dtype=q.dtype, device="cuda")[:, 1:]
+    new_out = torch.empty((3, n + 1), dtype=q.dtype, device="cuda")[:, 1:]
+    caches = [gc.prefill(g, 256) for g in range(2)]
+    tpla.rotate_append(qbig[:, 1:], q_out, nbig[:, 1:], gc.new_rope, gc.new_seq, gc.new_pos,
+                       caches, gc.bt, latent_out=new_out)
+    q_ref = torch.empty_like(q)
+    new_ref = torch.empty_like(gc.new_latent)
+    ref_caches = [gc.prefill(g, 256) for g in range(2)]
+    tpla.rotate_append(q, q_ref, gc.new_latent, gc.new_rope, gc.new_seq, gc.new_pos,
+                       ref_caches, gc.bt, latent_out=new_ref)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(q_out.contiguous()), _bits(q_ref))
+    assert np.array_equal(_bits(new_out.contiguous()), _bits(new_ref))
+    for c, r in zip(caches, ref_caches):
+        assert np.array_equal(_bits(c), _bits(r))
 
 
 def test_rotate_append_fp32_sources_and_skipped_rows():
