@@ -33,6 +33,11 @@ is taken:
 * The Hadamard matrix is Sylvester's, in natural order, scaled by 1/sqrt(n),
   applied to query and latent over the whole latent width, never to the rope
   (reading R4).
+* RMSNorm slicing ([BLOG] "How TPLA Works"): a device that holds one slice of
+  the rotated latent normalises that slice by the root mean square of the
+  slice alone (eps inside the root); the model's norm uses the whole vector.
+  The norm's gain is taken as folded into the weights that read the latent,
+  so both norms here are gain-free (reading R10).
 
 Every function works in float64.  bf16 data enter as their exact values.
 """
@@ -60,6 +65,9 @@ __all__ = [
     "tpla_decode_paged",
     "mla_decode",
     "mla_decode_unabsorbed",
+    "rms_normalize",
+    "slice_rms_normalize",
+    "rotate_normalize_latent",
 ]
 
 
@@ -334,3 +342,44 @@ def mla_decode_unabsorbed(q_nope, q_rope, c_lat, k_rope, w_uk, w_uv, scale: floa
         w = np.exp(s - s.max())
         out[h] = (w / w.sum()) @ vals
     return out
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm slicing ([BLOG] "How TPLA Works: Smart Slicing and
+# Reparameterization": a latent split across devices would be normalised
+# with only part of the data; an orthogonal transform applied before the
+# split makes those local statistics approximate the global ones.  [ABS-R]:
+# the reparameterisation of RMSNorm.)
+# ---------------------------------------------------------------------------
+
+def rms_normalize(y: np.ndarray, eps: float) -> np.ndarray:
+    """Global RMS norm over the last axis: y / sqrt(mean(y**2) + eps)."""
+    y = np.asarray(y, dtype=np.float64)
+    ms = np.mean(y * y, axis=-1, keepdims=True)
+    return y / np.sqrt(ms + eps)
+
+
+def slice_rms_normalize(y: np.ndarray, d_s: int, eps: float) -> np.ndarray:
+    """RMSNorm slicing: every block of d_s consecutive columns of the last
+    axis is divided by the RMS of that block alone (reading R10)."""
+    y = np.asarray(y, dtype=np.float64)
+    n = y.shape[-1]
+    if d_s < 1 or n % d_s != 0:
+        raise ValueError(f"slice width {d_s} must divide {n}")
+    blocks = y.reshape(*y.shape[:-1], n // d_s, d_s)
+    ms = np.mean(blocks * blocks, axis=-1, keepdims=True)
+    return (blocks / np.sqrt(ms + eps)).reshape(y.shape)
+
+
+def rotate_normalize_latent(x: np.ndarray, mode: str, d_s: int, eps: float,
+                            hadamard: bool = True) -> np.ndarray:
+    """The cached latent from the down-projected one: rotate (or not), then
+    normalise globally ("global"), per d_s slice ("slice") or not ("none")."""
+    y = fwht(x) if hadamard else np.asarray(x, dtype=np.float64)
+    if mode == "none":
+        return y
+    if mode == "global":
+        return rms_normalize(y, eps)
+    if mode == "slice":
+        return slice_rms_normalize(y, d_s, eps)
+    raise ValueError(f"unknown mode {mode!r}")

@@ -406,3 +406,88 @@ def test_paged_decode_matches_logical_decode():
             np.testing.assert_array_equal(o[b], ref_o)
             np.testing.assert_array_equal(lse[b], ref_l)
             off += n
+
+
+# --------------------------------------------------------------------------
+# RMSNorm slicing (global RMS norm vs per-slice RMS norm of the rotated latent)
+# --------------------------------------------------------------------------
+
+def test_rms_norm_closed_form_two_levels():
+    # slices of constant magnitude 1 and 3: the global RMS is sqrt(5), each
+    # slice's own RMS is its constant
+    x = np.array([1.0] * 256 + [-3.0] * 256)
+    g = oracle.rms_normalize(x, 0.0)
+    np.testing.assert_allclose(g[:256], 1 / math.sqrt(5), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(g[256:], -3 / math.sqrt(5), rtol=0, atol=1e-15)
+    s = oracle.slice_rms_normalize(x, 256, 0.0)
+    np.testing.assert_allclose(s, np.sign(x), rtol=0, atol=1e-15)
+    eps = 0.5
+    np.testing.assert_allclose(oracle.slice_rms_normalize(x, 256, eps)[:2], 1 / math.sqrt(1.5), rtol=1e-15)
+    np.testing.assert_allclose(oracle.slice_rms_normalize(x, 256, eps)[-1], -3 / math.sqrt(9.5), rtol=1e-15)
+
+
+@pytest.mark.parametrize("d_s", [512, 256, 128, 64])
+def test_rms_norm_matches_library(d_s):
+    x = _rng(d_s).standard_normal((5, 512)) * _rng(7).uniform(0.1, 10, size=(5, 1))
+    eps = 1e-6
+    ref_g = torch.nn.functional.rms_norm(torch.from_numpy(x), (512,), eps=eps).numpy()
+    np.testing.assert_allclose(oracle.rms_normalize(x, eps), ref_g, rtol=1e-13, atol=0)
+    ref_s = torch.nn.functional.rms_norm(torch.from_numpy(x).reshape(5, 512 // d_s, d_s), (d_s,),
+                                         eps=eps).reshape(5, 512).numpy()
+    np.testing.assert_allclose(oracle.slice_rms_normalize(x, d_s, eps), ref_s, rtol=1e-13, atol=0)
+
+
+def test_slice_rms_norm_brute_force_loops():
+    x = _rng(3).standard_normal((2, 16))
+    got = oracle.slice_rms_normalize(x, 4, 0.01)
+    for r in range(2):
+        for blk in range(4):
+            ss = 0.0
+            for k in range(4):
+                ss += x[r, 4 * blk + k] ** 2
+            den = math.sqrt(ss / 4 + 0.01)
+            for k in range(4):
+                assert abs(got[r, 4 * blk + k] - x[r, 4 * blk + k] / den) < 1e-14
+
+
+def test_rms_norm_invariants():
+    x = _rng(5).standard_normal((4, 512)) * 7.0
+    s = oracle.slice_rms_normalize(x, 128, 0.0)
+    np.testing.assert_allclose(np.mean(s.reshape(4, 4, 128) ** 2, axis=-1), 1.0, rtol=1e-13)
+    # the global norm commutes with the orthonormal transform; the per-slice
+    # norm in general does not
+    np.testing.assert_allclose(oracle.rms_normalize(oracle.fwht(x), 1e-6),
+                               oracle.fwht(oracle.rms_normalize(x, 1e-6)), rtol=1e-12, atol=1e-13)
+    assert not np.allclose(oracle.slice_rms_normalize(oracle.fwht(x), 128, 0.0),
+                           oracle.fwht(oracle.slice_rms_normalize(x, 128, 0.0)))
+    # the transform of a one-hot vector is flat, so every slice already has
+    # the global RMS: slice norm = global norm exactly
+    e = np.zeros(512)
+    e[37] = -4.0
+    y = oracle.fwht(e)
+    np.testing.assert_array_equal(oracle.slice_rms_normalize(y, 64, 0.0), oracle.rms_normalize(y, 0.0))
+    np.testing.assert_array_equal(oracle.rotate_normalize_latent(e, "slice", 64, 0.0),
+                                  oracle.rotate_normalize_latent(e, "global", 64, 0.0))
+    with pytest.raises(ValueError):
+        oracle.slice_rms_normalize(x, 100, 0.0)
+
+
+def test_rotation_before_slicing_shrinks_the_norm_gap():
+    # The transform spreads a few large channels over every slice, so the
+    # slice statistics approach the global one (the blog's argument for
+    # rotating before the split).  Latents with 4 outlier channels, all in
+    # the first 256-column slice.
+    rng = _rng(11)
+    x = rng.standard_normal((64, 512))
+    x[:, [3, 40, 100, 200]] *= 25.0
+    eps = 1e-6
+
+    def gap(hadamard):
+        g = oracle.rotate_normalize_latent(x, "global", 256, eps, hadamard=hadamard)
+        s = oracle.rotate_normalize_latent(x, "slice", 256, eps, hadamard=hadamard)
+        return np.linalg.norm(s - g, axis=-1) / np.linalg.norm(g, axis=-1)
+
+    plain, rotated = gap(False), gap(True)
+    assert np.median(plain) > 0.3
+    assert np.median(rotated) < 0.03
+    assert np.all(rotated < plain)
