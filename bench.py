@@ -58,6 +58,9 @@ def parse_args():
     ap.add_argument("--mode", default="step", choices=["step", "decode", "copy"])
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = auto)")
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--latent-norm", default="none", choices=["none", "global", "slice"],
+                    help="RMS norm of the rotated new latent inside rotate/append (slice = "
+                         "each shard's columns on their own)")
     ap.add_argument("--decode-launches", type=int, default=40)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's host timing (0 disables it)")
@@ -238,7 +241,7 @@ def main():
 
     def step(r):
         tpla.rotate_append(q_raw, q_rot, new_raw, new_rope, new_seq, new_pos, caches[r], bt,
-                           first_shard=shards[0])
+                           first_shard=shards[0], latent_norm=args.latent_norm)
         for i, g in enumerate(shards):
             decode(r, i, g)
 
@@ -336,6 +339,7 @@ def main():
                    "context": (list(cfg.ctx) if isinstance(cfg.ctx, tuple) else cfg.ctx),
                    "tokens_attended": lens_sum, "block_size": cfg.block_size,
                    "cache_replicas": replicas, "global_batch": B, "num_splits": splits,
+                   "latent_norm": args.latent_norm,
                    "seq_len": maxlen},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),

@@ -156,7 +156,17 @@ typedef struct tpla_rotate_append_args {
   const int32_t* block_table;  /* device int32 [batch, max_blocks_per_seq]      */
   int32_t max_blocks_per_seq;
   int32_t batch;
+  int32_t latent_norm;         /* TPLA_NORM_*: RMS norm of the rotated latent   */
+  float norm_eps;              /* > 0 when latent_norm != TPLA_NORM_NONE        */
 } tpla_rotate_append_args;
+
+/* RMS normalisation of the rotated new-token latent (tpla_rotate_append). */
+enum {
+  TPLA_NORM_NONE = 0,          /* the latent arrives normalised                 */
+  TPLA_NORM_GLOBAL = 1,        /* by the RMS of the whole rotated row           */
+  TPLA_NORM_SLICE = 2          /* each d_s slice by its own RMS (RMSNorm        */
+                               /*   slicing: one device's local statistics)     */
+};
 
 /*
  * tpla_rotate_append: the rotation of the query, the rotation of the new
@@ -168,16 +178,27 @@ typedef struct tpla_rotate_append_args {
  * Slicing and Reparameterization"), and each device caches only its latent
  * slice plus the rope (TPLA abstract).  With Hn = H_n / sqrt(n):
  *     q_out[r, :]      = q[r, :] . Hn                      r < q_rows
- *     c~               = latent[t, :] . Hn                 t < n_rows
+ *     c~               = N(latent[t, :] . Hn)              t < n_rows
  *     latent_out[t, :] = c~                                (if latent_out)
  *     caches[c][slot]  = [ c~[(first_shard+c)*d_s : +d_s] || rope[t, :] ]
  * with slot as in tpla_append_kv (rows with an out-of-range sequence,
- * position or block id are skipped).  Arithmetic and rounding are those of
- * tpla_hadamard_latent (float32, one round-to-nearest-even to the output
- * dtype); a rope of the cache's type is copied bit for bit.
+ * position or block id are skipped).  N is the identity (TPLA_NORM_NONE),
+ * y / sqrt(mean(y^2) + norm_eps) over the whole row (TPLA_NORM_GLOBAL), or
+ * the same over each block of d_s columns on its own (TPLA_NORM_SLICE):
+ * the RMSNorm slicing of the edgentiq blog's "How TPLA Works" section, in
+ * which a device normalises its latent slice with that slice's own
+ * statistics and the rotation before the split keeps them close to the
+ * global ones.  The norm's gain is left to the weights that read the
+ * latent.  Arithmetic and rounding are those of tpla_hadamard_latent
+ * (float32, one round-to-nearest-even to the output dtype, after the
+ * norm); a rope of the cache's type is copied bit for bit.  The query rows
+ * are never normalised.
  * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE (n not a power of two in
  * [64, 4096], strides shorter than a row, shards beyond n, n_caches outside
- * [0, 16], negative counts), TPLA_ERR_DTYPE.
+ * [0, 16], negative counts, latent_norm unknown, norm_eps not a positive
+ * finite number when a norm is asked for, TPLA_NORM_SLICE with d_s outside
+ * [1, n]), TPLA_ERR_UNSUPPORTED (TPLA_NORM_SLICE with d_s not a power of
+ * two or below n / 64), TPLA_ERR_DTYPE.
  */
 tpla_status tpla_rotate_append(const tpla_rotate_append_args* args, void* stream);
 

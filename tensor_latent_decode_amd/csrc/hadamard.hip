@@ -201,9 +201,11 @@ __global__ __launch_bounds__(256) void hadamard_kernel(const TIn* __restrict__ x
 
 // Steps a1-a3 of a decode step in one launch (n >= 64: one wave per row).
 // Waves [0, q_rows) rotate query rows; the next n_rows waves rotate a new
-// token's latent row, optionally store it, and write its shard slices and
-// its rope into the shard caches (paged, same rules as the append kernel).
-// Dtypes are wave-uniform run-time flags.
+// token's latent row, optionally RMS-normalise it (whole row, or each d_s
+// slice on its own: RMSNorm slicing, edgentiq blog "How TPLA Works"),
+// optionally store it, and write its shard slices and its rope into the
+// shard caches (paged, same rules as the append kernel).  Dtypes are
+// wave-uniform run-time flags.
 __device__ __forceinline__ float ld(const void* p, int64_t i, bool bf16) {
   return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
 }
@@ -249,16 +251,32 @@ __global__ __launch_bounds__(256) void rotate_append_kernel(RotateAppendParams p
   }
   const int64_t t = wave - p.q_rows;
   if (t >= p.n_rows) return;
-  // the row's page is looked up before the transform, so those dependent
-  // loads overlap the row load and the butterflies
-  const int b = p.row_seq[t];
-  const int pos = p.row_pos[t];
-  const bool placed = b >= 0 && b < p.batch && pos >= 0 && pos / p.block_size < p.max_blocks;
-  const int blk = placed ? p.bt[static_cast<int64_t>(b) * p.max_blocks + pos / p.block_size] : -1;
+  // The row's page is looked up before the transform, so those dependent
+  // loads overlap the row load and the butterflies.  Without caches the
+  // row tables and the paging sizes are not given (they may be NULL / 0).
+  int b = -1, pos = -1, blk = -1;
+  if (p.n_caches > 0) {
+    b = p.row_seq[t];
+    pos = p.row_pos[t];
+    const bool placed = b >= 0 && b < p.batch && pos >= 0 && pos / p.block_size < p.max_blocks;
+    blk = placed ? p.bt[static_cast<int64_t>(b) * p.max_blocks + pos / p.block_size] : -1;
+  }
   load_any<E>(p.lat, t * p.ls + e0, p.lat_bf16, p.lat_vec, v);
   fwht_row<E>(v, lane, 64);
 #pragma unroll
   for (int i = 0; i < E; ++i) v[i] *= norm;
+  if (p.norm != TPLA_NORM_NONE) {
+    // RMS over the whole row, or over this lane's d_s slice (d_s / E lanes,
+    // a power of two): a butterfly sum, bit-identical in every lane.
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) ss = fmaf(v[i], v[i], ss);
+    const int group = p.norm == TPLA_NORM_GLOBAL ? 64 : p.d_s / E;
+    for (int m = 1; m < group; m <<= 1) ss += __shfl_xor(ss, m, 64);
+    const float r = 1.0f / sqrtf(ss / static_cast<float>(group * E) + p.norm_eps);
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] *= r;
+  }
   if (p.lat_out != nullptr) store_any<E>(p.lat_out, t * p.los + e0, p.lat_bf16, p.lat_vec, v);
   if (blk < 0 || blk >= p.num_blocks) return;
   const int width = p.d_s + p.d_r;

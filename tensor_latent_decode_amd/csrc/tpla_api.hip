@@ -310,6 +310,14 @@ tpla_status tpla_rotate_append(const tpla_rotate_append_args* a, void* stream) {
   if (a->q_rows < 0 || a->n_rows < 0) return fail(TPLA_ERR_SHAPE, "q_rows and n_rows must be >= 0");
   if (a->n_caches < 0 || a->n_caches > tpla::kMaxTp)
     return fail(TPLA_ERR_SHAPE, "n_caches must be in [0, %d]", tpla::kMaxTp);
+  if (a->latent_norm < TPLA_NORM_NONE || a->latent_norm > TPLA_NORM_SLICE)
+    return fail(TPLA_ERR_SHAPE, "latent_norm=%d is not a TPLA_NORM_* value", a->latent_norm);
+  if (a->latent_norm != TPLA_NORM_NONE && !(std::isfinite(a->norm_eps) && a->norm_eps > 0.f))
+    return fail(TPLA_ERR_SHAPE, "norm_eps must be a positive finite number");
+  if (a->latent_norm == TPLA_NORM_SLICE && (a->d_s < 1 || a->d_s > n))
+    return fail(TPLA_ERR_SHAPE, "slice norm: d_s=%d must be in [1, n=%d]", a->d_s, n);
+  if (a->latent_norm == TPLA_NORM_SLICE && (!is_pow2(a->d_s) || a->d_s < n / 64))
+    return fail(TPLA_ERR_UNSUPPORTED, "slice norm needs d_s a power of two >= n/64, got %d", a->d_s);
   if (a->q_rows > 0) {
     if (a->q == nullptr || a->q_out == nullptr) return fail(TPLA_ERR_NULL, "q and q_out are required");
     if (a->q_row_stride < n || a->q_out_row_stride < n)
@@ -367,6 +375,8 @@ tpla_status tpla_rotate_append(const tpla_rotate_append_args* a, void* stream) {
   p.max_blocks = a->max_blocks_per_seq;
   p.batch = a->batch;
   p.bt = a->block_table;
+  p.norm = a->latent_norm;
+  p.norm_eps = a->norm_eps;
   return hip_status(tpla::launch_rotate_append(p, n, static_cast<hipStream_t>(stream)),
                     "rotate/append launch");
 }

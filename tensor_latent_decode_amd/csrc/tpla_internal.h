@@ -108,6 +108,8 @@ struct RotateAppendParams {
   int n_caches, first_shard, cache_bf16;
   int num_blocks, block_size, d_s, d_r, max_blocks, batch;
   const int32_t* bt;
+  int norm;                     // TPLA_NORM_* of the rotated latent rows
+  float norm_eps;
 };
 
 // Launchers (return the launch status; they do not synchronise).

@@ -67,8 +67,11 @@ class RotateAppendArgs(ctypes.Structure):
         ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32), ("d_s", ctypes.c_int32),
         ("d_r", ctypes.c_int32), ("block_table", ctypes.c_void_p),
         ("max_blocks_per_seq", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("latent_norm", ctypes.c_int32), ("norm_eps", ctypes.c_float),
     ]
 
+
+NORMS = {"none": 0, "global": 1, "slice": 2}   # TPLA_NORM_*
 
 _lib = None
 
@@ -206,11 +209,16 @@ def rotate_append(q: Optional[torch.Tensor], q_out: Optional[torch.Tensor],
                   row_seq: Optional[torch.Tensor] = None, row_pos: Optional[torch.Tensor] = None,
                   caches: Sequence[torch.Tensor] = (), block_table: Optional[torch.Tensor] = None,
                   first_shard: int = 0, latent_out: Optional[torch.Tensor] = None,
-                  batch: Optional[int] = None) -> None:
+                  batch: Optional[int] = None, latent_norm: str = "none", norm_eps: float = 1e-6,
+                  slice_width: Optional[int] = None) -> None:
     """One launch: q_out = q . H_n/sqrt(n) over the last dim; the new latent
-    rows rotated the same way (into latent_out if given) and their shard
-    slices first_shard, first_shard+1, ... appended with the rope into
-    `caches` (each [num_blocks, block_size, d_s + d_r])."""
+    rows rotated the same way, RMS-normalised per `latent_norm` ("none",
+    "global": the whole row, "slice": each slice_width-column slice on its
+    own; slice_width defaults to the caches' d_s), stored into latent_out if
+    given, and their shard slices first_shard, first_shard+1, ... appended
+    with the rope into `caches` (each [num_blocks, block_size, d_s + d_r])."""
+    if latent_norm not in NORMS:
+        raise ValueError(f"latent_norm must be one of {sorted(NORMS)}")
     _gpu(q, q_out, latent, rope, row_seq, row_pos, block_table, latent_out, *caches)
     a = RotateAppendArgs()
     n = None
@@ -267,6 +275,13 @@ def rotate_append(q: Optional[torch.Tensor], q_out: Optional[torch.Tensor],
     if n is None:
         return
     a.n = n
+    a.latent_norm, a.norm_eps = NORMS[latent_norm], norm_eps
+    if slice_width is not None:
+        if caches and slice_width != a.d_s:
+            raise ValueError("slice_width must equal the caches' d_s")
+        a.d_s = slice_width
+    elif latent_norm == "slice" and not caches:
+        raise ValueError("the slice norm needs slice_width or caches")
     dev_t = q if q is not None else latent
     _check("tpla_rotate_append", lib().tpla_rotate_append(ctypes.byref(a), _stream(dev_t)))
 

@@ -103,6 +103,12 @@ def test_rotate_append_argument_checks():
         a, keep = _rot_args()
         setattr(a, field, value)
         _fails(call(a), code)
+    for norm, eps, d_s, code in [(3, 1e-6, 256, 2), (-1, 1e-6, 256, 2), (1, 0.0, 256, 2),
+                                 (2, float("nan"), 256, 2), (1, float("inf"), 256, 2),
+                                 (2, 1e-6, 100, 5), (2, 1e-6, 4, 5), (2, 1e-6, 1024, 2)]:
+        a, keep = _rot_args()
+        a.latent_norm, a.norm_eps, a.d_s = norm, eps, d_s
+        _fails(call(a), code)
     a, keep = _rot_args()
     keep[1] = None                                   # caches[1] is NULL
     _fails(call(a), 1)

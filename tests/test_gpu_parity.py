@@ -221,6 +221,66 @@ def test_rotate_append_unaligned_rows_match_aligned():
         assert np.array_equal(_bits(c), _bits(r))
 
 
+@pytest.mark.parametrize("cfg", ["dsv3_4k", "kimi_k2_32k"])
+@pytest.mark.parametrize("mode", ["global", "slice"])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_rotate_append_latent_norm(cfg, mode, dt):
+    # new latent rows with outlier channels, RMS-normalised after the rotation
+    # over the whole row or per shard slice (RMSNorm slicing), against the
+    # oracle; the caches get exactly the stored slices; the query is
+    # untouched by the norm
+    case = make_case(CONFIGS[cfg], batch=4, ctx=(30, 200), seed=29, heads=32)
+    gc = GpuCase(case)
+    d_s, tp, n = case.cfg.d_s, case.cfg.tp, case.cfg.d_c
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((4, n)).astype(np.float32) * 3.0
+    x[:, [5, 77, 130, 300]] *= 20.0
+    x[1] *= 1e-3                                           # small row: eps matters little
+    lat = torch.from_numpy(x).cuda().to(dt)
+    rope = gc.new_rope.to(dt)
+    eps = 1e-6
+    lat_out = torch.empty_like(lat)
+    caches = [gc.prefill(g, d_s) if dt == torch.bfloat16 else None for g in range(tp)]
+    caches = [c for c in caches if c is not None]
+    q_out = torch.empty_like(gc.q_latent)
+    tpla.rotate_append(gc.q_latent, q_out, lat, rope, gc.new_seq, gc.new_pos, caches, gc.bt,
+                       latent_out=lat_out, latent_norm=mode, norm_eps=eps,
+                       slice_width=None if caches else d_s)
+    q_ref = torch.empty_like(gc.q_latent)
+    tpla.rotate_append(gc.q_latent, q_ref, None, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(q_out), _bits(q_ref))
+    ref = oracle.rotate_normalize_latent(host_f64(lat), mode, d_s, eps)
+    got = host_f64(lat_out)
+    if dt == torch.bfloat16:   # one rounding of a float32 result: within one bf16 ulp
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30), float(np.max(np.abs(got - ref)))
+    else:
+        assert rel_err(got, ref) <= TOL_FP32
+    if mode == "slice":   # rows where eps is negligible: every slice has unit mean square
+        ms = np.mean(got.reshape(4, tp, d_s)[[0, 2, 3]] ** 2, axis=-1)
+        np.testing.assert_allclose(ms, 1.0, rtol=1e-2)
+    bits = _bits(lat_out)
+    for g, c in enumerate(caches):
+        cb = _bits(c)
+        for b in range(4):
+            p = int(case.new_pos[b])
+            row = cb[int(case.block_table[b, p // 64]), p % 64]
+            assert np.array_equal(row[:d_s], bits[b, g * d_s:(g + 1) * d_s])
+
+
+def test_rotate_append_slice_norm_without_caches_and_checks():
+    lat = torch.randn(3, 512, device="cuda")
+    out = torch.empty_like(lat)
+    tpla.rotate_append(None, None, lat, None, latent_out=out, latent_norm="slice", slice_width=128)
+    torch.cuda.synchronize()
+    ref = oracle.rotate_normalize_latent(host_f64(lat), "slice", 128, 1e-6)
+    assert rel_err(host_f64(out), ref) <= TOL_FP32
+    with pytest.raises(tpla.TplaError):
+        tpla.rotate_append(None, None, lat, None, latent_out=out, latent_norm="slice", slice_width=4)
+    with pytest.raises(tpla.TplaError):
+        tpla.rotate_append(None, None, lat, None, latent_out=out, latent_norm="global", norm_eps=0.0)
+
+
 def test_rotate_append_fp32_sources_and_skipped_rows():
     case = make_case(CONFIGS["dsv3_4k"], batch=4, ctx=(10, 80), seed=19, heads=32)
     gc = GpuCase(case)
