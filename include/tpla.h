@@ -280,14 +280,21 @@ tpla_status tpla_decode_suggest_splits(const tpla_decode_args* args, const int32
  * (online softmax) and the splits are merged by log-sum-exp before `out` is
  * written.
  *
- * Requirements: dtype BF16 with heads % 32 == 0, d_s % 32 == 0, d_r % 16 == 0,
- * 16-byte aligned q/cache pointers and strides that are multiples of 8 use
- * the bf16 matrix-core kernel; every other shape (and FP32) runs a plain
- * float32 kernel.  d_s + d_r <= 1024.  out_dtype FP32 or BF16.
+ * Kernels: with dtype BF16, 16-byte aligned q_latent/q_rope/cache and query
+ * strides that are multiples of 8,
+ *   - the streaming matrix-core kernel serves block_size % 64 == 0, d_r == 64
+ *     and either heads % 128 == 0 with d_s == 256 or heads % 64 == 0 with
+ *     d_s == 128;
+ *   - a register-staged matrix-core kernel serves heads % 32 == 0 with d_s
+ *     in {64, 128, 256} and d_r in {0, 64};
+ * every other case (and FP32) runs a float32 kernel, which needs
+ * 4*(24*(d_s + d_r) + 8*d_s + 152) <= 65536 bytes of LDS (e.g. d_s = 256,
+ * d_r = 64 fits; d_s = 512, d_r = 64 does not: TPLA_ERR_UNSUPPORTED).
+ * out_dtype FP32 or BF16.
  * workspace: device, at least tpla_decode_workspace_size() bytes, 256-byte
  * aligned; its contents on entry do not matter.
- * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE, TPLA_ERR_DTYPE, TPLA_ERR_WORKSPACE,
- * TPLA_ERR_HIP.
+ * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE, TPLA_ERR_DTYPE, TPLA_ERR_UNSUPPORTED
+ * (no kernel for the shape, above), TPLA_ERR_WORKSPACE, TPLA_ERR_HIP.
  */
 tpla_status tpla_decode_shard(const tpla_decode_args* args, void* workspace,
                               size_t workspace_bytes, void* stream);

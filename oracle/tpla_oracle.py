@@ -38,6 +38,10 @@ is taken:
   slice alone (eps inside the root); the model's norm uses the whole vector.
   The norm's gain is taken as folded into the weights that read the latent,
   so both norms here are gain-free (reading R10).
+* The all-reduce sums real arithmetic once each device applies its slice of
+  the value up-projection: device g holds rows g*d_s .. of every head's
+  transposed W_UV (latent index first), rotated like the latent, and its
+  up-projected output is summed over devices (reading R11).
 
 Every function works in float64.  bf16 data enter as their exact values.
 """
@@ -68,6 +72,9 @@ __all__ = [
     "rms_normalize",
     "slice_rms_normalize",
     "rotate_normalize_latent",
+    "up_project_shard",
+    "up_project_combine",
+    "rotate_weight_rows",
 ]
 
 
@@ -383,3 +390,44 @@ def rotate_normalize_latent(x: np.ndarray, mode: str, d_s: int, eps: float,
     if mode == "slice":
         return slice_rms_normalize(y, d_s, eps)
     raise ValueError(f"unknown mode {mode!r}")
+
+
+# ---------------------------------------------------------------------------
+# Value up-projection per shard and the all-reduce sum ([ABS]: each shard's
+# attention runs on its own and the results are combined with an
+# all-reduce; [ABS-R]: the orthogonal reparameterisation keeps MLA's
+# weights usable).  In MLA the head-h value of token t is W_UV[h] @ c_t, so
+# head h's output is W_UV[h] @ (sum_t p_t c_t): the latent-space output
+# times the head's W_UV.
+# ---------------------------------------------------------------------------
+
+def up_project_shard(o_shard: np.ndarray, w_shard: np.ndarray) -> np.ndarray:
+    """One device's up-projected output: y[b, h, :] = o[b, h, :] @ w[h].
+
+    o_shard [B, H, d_s] (this device's latent-space attention output),
+    w_shard [H, d_s, d_v] (its rows of every head's transposed W_UV).
+    """
+    o = np.asarray(o_shard, dtype=np.float64)
+    w = np.asarray(w_shard, dtype=np.float64)
+    # per head: [B, d_s] @ [d_s, d_v]
+    return np.matmul(o.transpose(1, 0, 2), w).transpose(1, 0, 2)
+
+
+def up_project_combine(o_shards, w_shards) -> np.ndarray:
+    """The all-reduce: sum over devices of up_project_shard (reading R11)."""
+    parts = [up_project_shard(o, w) for o, w in zip(o_shards, w_shards)]
+    out = np.zeros_like(parts[0])
+    for y in parts:
+        out = out + y
+    return out
+
+
+def rotate_weight_rows(w_t: np.ndarray) -> np.ndarray:
+    """Transposed W_UV [H, d_c, d_v] for a latent rotated by Hn: Hn @ w_t[h].
+
+    With c~ = c @ Hn the latent-space output is o~ = o @ Hn, and
+    o @ w_t = o~ @ (Hn^T @ w_t) = o~ @ (Hn @ w_t) since Hn is symmetric and
+    orthonormal.  Hn @ w_t[h] is the transform applied along the d_c axis.
+    """
+    w = np.asarray(w_t, dtype=np.float64)
+    return fwht(w.transpose(0, 2, 1)).transpose(0, 2, 1)

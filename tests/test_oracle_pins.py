@@ -491,3 +491,59 @@ def test_rotation_before_slicing_shrinks_the_norm_gap():
     assert np.median(plain) > 0.3
     assert np.median(rotated) < 0.03
     assert np.all(rotated < plain)
+
+
+# --------------------------------------------------------------------------
+# Value up-projection per shard and the summing all-reduce
+# --------------------------------------------------------------------------
+
+def test_up_project_at_one_shard_equals_unabsorbed_mla():
+    # T = 1, no rotation: the up-projected latent-space output is exactly
+    # MLA with explicit per-head values (W_UV applied to every cached row)
+    rng = _rng(41)
+    H, d_n, d_c, d_r, d_v, L = 3, 16, 32, 8, 12, 40
+    q_nope, q_rope = rng.standard_normal((H, d_n)), rng.standard_normal((H, d_r))
+    c, r = rng.standard_normal((L, d_c)), rng.standard_normal((L, d_r))
+    w_uk = rng.standard_normal((H, d_n, d_c)) / 4
+    w_uv = rng.standard_normal((H, d_v, d_c)) / 4
+    scale = 1 / math.sqrt(d_n + d_r)
+    ref = oracle.mla_decode_unabsorbed(q_nope, q_rope, c, r, w_uk, w_uv, scale)
+    q_lat = np.stack([w_uk[h].T @ q_nope[h] for h in range(H)])
+    (o, _), = oracle.tpla_shards(q_lat, q_rope, c, r, 1, scale, hadamard=False)
+    y = oracle.up_project_shard(o[None], w_uv.transpose(0, 2, 1))[0]
+    np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_up_project_brute_force_and_shard_sum():
+    rng = _rng(43)
+    B, H, d_c, d_v, T = 2, 3, 8, 5, 2
+    o = rng.standard_normal((B, H, d_c))
+    w = rng.standard_normal((H, d_c, d_v))
+    got = oracle.up_project_shard(o, w)
+    for b in range(B):
+        for h in range(H):
+            for v in range(d_v):
+                acc = 0.0
+                for k in range(d_c):
+                    acc += o[b, h, k] * w[h, k, v]
+                assert abs(got[b, h, v] - acc) < 1e-12
+    # the sum over devices of slice products is the product over the whole
+    # latent: the all-reduce reassembles the un-split contraction
+    d_s = d_c // T
+    parts_o = [o[..., g * d_s:(g + 1) * d_s] for g in range(T)]
+    parts_w = [w[:, g * d_s:(g + 1) * d_s, :] for g in range(T)]
+    np.testing.assert_allclose(oracle.up_project_combine(parts_o, parts_w), got, rtol=1e-13, atol=1e-13)
+
+
+def test_rotated_weights_undo_the_latent_rotation():
+    # o @ w == (o @ Hn) @ (Hn @ w): the rotation applied to latent and query
+    # is absorbed into W_UV's latent rows
+    rng = _rng(47)
+    o = rng.standard_normal((4, 3, 64))
+    w = rng.standard_normal((3, 64, 7))
+    y = oracle.up_project_shard(o, w)
+    y_rot = oracle.up_project_shard(oracle.fwht(o), oracle.rotate_weight_rows(w))
+    np.testing.assert_allclose(y_rot, y, rtol=1e-12, atol=1e-12)
+    # rotate_weight_rows is Hn @ w[h] with the dense library matrix
+    Hn = scipy.linalg.hadamard(64) / 8.0
+    np.testing.assert_allclose(oracle.rotate_weight_rows(w)[1], Hn @ w[1], rtol=1e-13, atol=1e-13)
