@@ -255,7 +255,7 @@ const char* tpla_status_string(tpla_status s) {
 
 const char* tpla_last_error(void) { return g_err; }
 
-int32_t tpla_version(void) { return 200; }
+int32_t tpla_version(void) { return 300; }
 
 tpla_status tpla_hadamard_latent(const void* x, tpla_dtype x_dtype, int64_t x_row_stride, void* y,
                                  tpla_dtype y_dtype, int64_t y_row_stride, int64_t rows, int32_t n,
@@ -455,6 +455,42 @@ tpla_status tpla_decode_shard(const tpla_decode_args* a, void* workspace, size_t
   m.out_sh = a->out_stride_h;
   m.lse = a->lse;
   return hip_status(tpla::launch_merge(m, s), "merge launch");
+}
+
+tpla_status tpla_up_project(const void* o, tpla_dtype o_dtype, int64_t o_stride_b,
+                            int64_t o_stride_h, const void* w, tpla_dtype w_dtype,
+                            int64_t w_stride_h, int64_t w_stride_k, void* y, tpla_dtype y_dtype,
+                            int64_t y_stride_b, int64_t y_stride_h, int32_t batch, int32_t heads,
+                            int32_t d_s, int32_t d_v, int32_t accumulate, void* stream) {
+  if (!valid_dtype(o_dtype) || !valid_dtype(w_dtype) || !valid_dtype(y_dtype))
+    return fail(TPLA_ERR_DTYPE, "dtypes must be TPLA_FP32 or TPLA_BF16");
+  if (batch < 1 || heads < 1 || d_s < 1 || d_v < 1)
+    return fail(TPLA_ERR_SHAPE, "batch, heads, d_s, d_v must be >= 1");
+  if (heads > 65535) return fail(TPLA_ERR_SHAPE, "heads=%d exceeds 65535", heads);
+  if (o_stride_h < d_s || w_stride_k < d_v || w_stride_h < static_cast<int64_t>(d_s) * w_stride_k ||
+      y_stride_h < d_v || o_stride_b < 0 || y_stride_b < 0)
+    return fail(TPLA_ERR_SHAPE, "strides must cover a row");
+  if (d_s > tpla::kMaxUpProjectK)
+    return fail(TPLA_ERR_UNSUPPORTED, "d_s=%d exceeds %d", d_s, tpla::kMaxUpProjectK);
+  if (o == nullptr || w == nullptr || y == nullptr) return fail(TPLA_ERR_NULL, "o, w and y are required");
+  tpla::UpProjectParams p{};
+  p.o = o;
+  p.o_sb = o_stride_b;
+  p.o_sh = o_stride_h;
+  p.w = w;
+  p.w_sh = w_stride_h;
+  p.w_sk = w_stride_k;
+  p.y = y;
+  p.y_sb = y_stride_b;
+  p.y_sh = y_stride_h;
+  p.batch = batch;
+  p.heads = heads;
+  p.d_s = d_s;
+  p.d_v = d_v;
+  p.accumulate = accumulate != 0;
+  return hip_status(tpla::launch_up_project(p, o_dtype == TPLA_BF16, w_dtype == TPLA_BF16,
+                                            y_dtype == TPLA_BF16, static_cast<hipStream_t>(stream)),
+                    "up-projection launch");
 }
 
 tpla_status tpla_combine_shards(const void* const* partials, tpla_dtype part_dtype, int32_t tp,

@@ -112,7 +112,22 @@ struct RotateAppendParams {
   float norm_eps;
 };
 
+// Value up-projection: y[b, h, v] (+)= sum_k o[b, h, k] * w[h, k, v].
+constexpr int kMaxUpProjectK = 1024;   // d_s limit (the head's rows of o are staged in LDS)
+struct UpProjectParams {
+  const void* o;
+  int64_t o_sb, o_sh;
+  const void* w;
+  int64_t w_sh, w_sk;
+  void* y;
+  int64_t y_sb, y_sh;
+  int batch, heads, d_s, d_v;
+  int accumulate;
+};
+
 // Launchers (return the launch status; they do not synchronise).
+hipError_t launch_up_project(const UpProjectParams& p, bool o_bf16, bool w_bf16, bool y_bf16,
+                             hipStream_t s);
 hipError_t launch_hadamard(const void* x, int x_bf16, int64_t xs, void* y, int y_bf16, int64_t ys,
                            int64_t rows, int n, hipStream_t s);
 hipError_t launch_rotate_append(const RotateAppendParams& p, int n, hipStream_t s);

@@ -95,9 +95,11 @@ def lib() -> ctypes.CDLL:
     L.tpla_combine_shards.argtypes = [ctypes.POINTER(vp), dt, i32, i32, i32, i32, vp, dt, i32, vp]
     L.tpla_rotate_append.argtypes = [ctypes.POINTER(RotateAppendArgs), vp]
     L.tpla_decode_suggest_splits.argtypes = [ctypes.POINTER(DecodeArgs), vp, ctypes.POINTER(i32)]
+    L.tpla_up_project.argtypes = [vp, dt, i64, i64, vp, dt, i64, i64, vp, dt, i64, i64,
+                                  i32, i32, i32, i32, i32, vp]
     for f in ("tpla_hadamard_latent", "tpla_append_kv", "tpla_decode_workspace_size",
               "tpla_decode_shard", "tpla_combine_shards", "tpla_rotate_append",
-              "tpla_decode_suggest_splits"):
+              "tpla_decode_suggest_splits", "tpla_up_project"):
         getattr(L, f).restype = ctypes.c_int
     L.tpla_status_string.argtypes = [ctypes.c_int]
     L.tpla_status_string.restype = ctypes.c_char_p
@@ -284,6 +286,32 @@ def rotate_append(q: Optional[torch.Tensor], q_out: Optional[torch.Tensor],
         raise ValueError("the slice norm needs slice_width or caches")
     dev_t = q if q is not None else latent
     _check("tpla_rotate_append", lib().tpla_rotate_append(ctypes.byref(a), _stream(dev_t)))
+
+
+def up_project(o: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,
+               accumulate: bool = False, out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """out[b, h, :] (+)= o[b, h, :] @ w[h] for o [B, H, d_s] and w [H, d_s, d_v]
+    (one device's rows of every head's transposed W_UV); accumulate=True adds
+    into `out`, which is how the shards' terms are summed on one device."""
+    _gpu(o, w, out)
+    if o.dim() != 3 or w.dim() != 3 or o.stride(-1) != 1 or w.stride(-1) != 1:
+        raise ValueError("o must be [B, H, d_s] and w [H, d_s, d_v] with contiguous last dims")
+    B, H, d_s = o.shape
+    if w.shape[0] != H or w.shape[1] != d_s:
+        raise ValueError("w must be [H, d_s, d_v] matching o")
+    d_v = w.shape[2]
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs out")
+        out = torch.empty((B, H, d_v), dtype=out_dtype or torch.float32, device=o.device)
+    if out.shape != (B, H, d_v) or out.stride(-1) != 1:
+        raise ValueError("out must be [B, H, d_v] with a contiguous last dim")
+    _check("tpla_up_project",
+           lib().tpla_up_project(o.data_ptr(), _dt(o), o.stride(0), o.stride(1),
+                                 w.data_ptr(), _dt(w), w.stride(0), w.stride(1),
+                                 out.data_ptr(), _dt(out), out.stride(0), out.stride(1),
+                                 B, H, d_s, d_v, int(accumulate), _stream(o)))
+    return out
 
 
 def make_decode_args(q_latent: torch.Tensor, q_rope: Optional[torch.Tensor], cache: torch.Tensor,

@@ -19,7 +19,7 @@ def test_exports_every_declared_function():
     assert {"tpla_hadamard_latent", "tpla_append_kv", "tpla_decode_workspace_size",
             "tpla_decode_shard", "tpla_combine_shards", "tpla_status_string",
             "tpla_last_error", "tpla_version", "tpla_rotate_append",
-            "tpla_decode_suggest_splits"} <= set(names)
+            "tpla_decode_suggest_splits", "tpla_up_project"} <= set(names)
     raw = ctypes.CDLL(tpla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -27,7 +27,7 @@ def test_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = tpla.lib()
-    assert tpla.version() == 200
+    assert tpla.version() == 300
     for code in range(8):
         assert L.tpla_status_string(code)
     assert L.tpla_status_string(99) == b"unknown status"
@@ -205,3 +205,30 @@ def test_suggest_splits_argument_checks():
     a.d_s = 0
     _fails(L.tpla_decode_suggest_splits(ctypes.byref(a), ctypes.cast(lens, ctypes.c_void_p),
                                         ctypes.byref(out)), 2)
+
+
+def test_up_project_argument_checks():
+    L = tpla.lib()
+    base = [FAKE, 1, 128 * 256, 256, FAKE, 1, 256 * 128, 128, FAKE, 0, 128 * 128, 128,
+            16, 128, 256, 128, 0, None]
+    def call(**kw):
+        args = list(base)
+        names = ["o", "o_dt", "o_sb", "o_sh", "w", "w_dt", "w_sh", "w_sk", "y", "y_dt", "y_sb",
+                 "y_sh", "batch", "heads", "d_s", "d_v", "acc", "stream"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return L.tpla_up_project(*args)
+    _fails(call(o_dt=5), 4)
+    _fails(call(y_dt=7), 4)
+    _fails(call(batch=0), 2)
+    _fails(call(d_v=0), 2)
+    _fails(call(heads=70000, w_sh=256 * 128), 2)
+    _fails(call(o_sh=100), 2)                  # head stride shorter than d_s
+    _fails(call(w_sk=64), 2)                   # row stride shorter than d_v
+    _fails(call(w_sh=1000), 2)                 # head stride shorter than d_s rows
+    _fails(call(y_sh=64), 2)
+    _fails(call(o_sb=-1), 2)
+    _fails(call(d_s=2048, o_sh=2048, w_sh=2048 * 128), 5)
+    _fails(call(o=None), 1)
+    _fails(call(w=None), 1)
+    _fails(call(y=None), 1)

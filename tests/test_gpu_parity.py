@@ -618,3 +618,72 @@ def test_ragged_tp2_full_step_sampled():
     for b in (int(order[0]), int(order[-1]), 7):
         ref, _ = oracle_step(case, b, 2, hadamard=True)
         assert rel_err(got[b], ref) <= TOL_BF16, (b, int(case.seq_lens[b]))
+
+
+# --------------------------------------------------------------------------
+# Value up-projection per shard and the summing all-reduce
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,H,d_s,d_v", [(16, 128, 256, 128), (20, 8, 200, 100), (1, 3, 1024, 70),
+                                         (33, 2, 64, 257)])
+@pytest.mark.parametrize("dts", [("f32", "bf16", "f32"), ("bf16", "bf16", "bf16"), ("f32", "f32", "f32")])
+def test_up_project_parity(B, H, d_s, d_v, dts):
+    # several batch passes (B > 16), partial column blocks, d_s not a
+    # multiple of four, strided o (a column slice of a wider output)
+    rng = np.random.default_rng(B * 1000 + d_s)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    wide = torch.from_numpy(rng.standard_normal((B, H, d_s + 7)).astype(np.float32)).cuda()
+    o = wide[:, :, 3:3 + d_s].to(tdt[dts[0]]) if dts[0] == "bf16" else wide[:, :, 3:3 + d_s]
+    w = torch.from_numpy((rng.standard_normal((H, d_s, d_v)) / 16).astype(np.float32)).cuda().to(tdt[dts[1]])
+    y = tpla.up_project(o, w, out_dtype=tdt[dts[2]])
+    torch.cuda.synchronize()
+    ref = oracle.up_project_shard(host_f64(o), host_f64(w))
+    tol = TOL_BF16 if dts[2] == "bf16" else TOL_FP32
+    assert rel_err(host_f64(y), ref) <= tol
+
+
+def test_up_project_accumulates_shards():
+    # two devices' terms summed into one output equal the oracle's all-reduce
+    rng = np.random.default_rng(5)
+    B, H, d_s, d_v, T = 16, 16, 256, 128, 2
+    os_ = [torch.from_numpy(rng.standard_normal((B, H, d_s)).astype(np.float32)).cuda() for _ in range(T)]
+    ws = [torch.from_numpy((rng.standard_normal((H, d_s, d_v)) / 16).astype(np.float32)).cuda()
+          .to(torch.bfloat16) for _ in range(T)]
+    y = tpla.up_project(os_[0], ws[0])
+    tpla.up_project(os_[1], ws[1], out=y, accumulate=True)
+    y1 = tpla.up_project(os_[1], ws[1])
+    torch.cuda.synchronize()
+    ref = oracle.up_project_combine([host_f64(o) for o in os_], [host_f64(w) for w in ws])
+    assert rel_err(host_f64(y), ref) <= TOL_FP32
+    # the second call added its own result to the first one's, in float32
+    y0 = tpla.up_project(os_[0], ws[0])
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0 + y1)
+
+
+@pytest.mark.parametrize("hadamard", [False, True])
+def test_full_step_with_up_projection(hadamard):
+    # decode both shards, up-project each with its rows of the (rotated)
+    # transposed W_UV and sum: against the oracle's TPLA step followed by
+    # its up-projection and all-reduce
+    case = make_case(CONFIGS["dsv3_4k"], batch=3, ctx=(200, 900), seed=83, heads=32)
+    gc = GpuCase(case)
+    cfg = case.cfg
+    d_s, d_v = cfg.d_s, 128
+    rng = np.random.default_rng(89)
+    w_t = rng.standard_normal((cfg.heads, cfg.d_c, d_v)) / 16          # [H, d_c, d_v]
+    w_dev = np.ascontiguousarray(oracle.rotate_weight_rows(w_t) if hadamard else w_t)
+    _, outs, _ = run_step(gc, hadamard)
+    w_gpu = torch.from_numpy(w_dev.astype(np.float32)).cuda().to(torch.bfloat16)
+    y = None
+    for g in range(cfg.tp):
+        wg = w_gpu[:, g * d_s:(g + 1) * d_s, :]
+        y = tpla.up_project(outs[g], wg, out=y, accumulate=g > 0)
+    torch.cuda.synchronize()
+    w_used = host_f64(w_gpu)           # the bf16 weights as the kernel saw them
+    for b in range(cfg.batch):
+        _, parts = oracle_step(case, b, cfg.tp, hadamard=hadamard)
+        o_sh = [p[0][None] for p in parts]
+        w_sh = [w_used[:, g * d_s:(g + 1) * d_s, :] for g in range(cfg.tp)]
+        ref = oracle.up_project_combine(o_sh, w_sh)[0]
+        assert rel_err(host_f64(y)[b], ref) <= TOL_BF16, b
