@@ -10,6 +10,9 @@ what tpla_hadamard_latent and tpla_append_kv do separately), decode the shard
 (tpla_decode_shard: split-K attention and log-sum-exp merge) and combine the
 shard outputs: every shard's merge writes its latent columns of the combined
 output (the placement tpla_combine_shards performs for outputs held apart).
+`--up-project D_V` adds each shard's value up-projection (tpla_up_project,
+random bf16 weights) with the shards' terms summed; `--latent-norm` adds the
+RMS norm of the new latent to the append.
 The default workload is the DeepSeek-V3-shaped shard at 32K context
 (B=16, H=128, d_c=512 split TP=2 -> d_s=256, d_r=64, paged blocks of 64 with
 a permuted block table); `--workload ragged_tp2` runs both shards of the
@@ -62,6 +65,9 @@ def parse_args():
     ap.add_argument("--mode", default="step", choices=["step", "decode", "copy"])
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = auto)")
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--up-project", type=int, default=0, metavar="D_V",
+                    help="add each shard's value up-projection to the step (random bf16 "
+                         "weights, D_V output columns per head; the shards' terms are summed)")
     ap.add_argument("--latent-norm", default="none", choices=["none", "global", "slice"],
                     help="RMS norm of the rotated new latent inside rotate/append (slice = "
                          "each shard's columns on their own)")
@@ -243,11 +249,23 @@ def main():
                           cfg.scale, maxlen, out=outs[i], lse=lses[i], num_splits=splits,
                           workspace=workspace)
 
+    # optional value up-projection: each shard's rows of every head's
+    # transposed W_UV (synthetic, seeded), the shards' terms summed into y
+    w_up, y_up = [], None
+    if args.up_project:
+        gen = torch.Generator(device="cpu").manual_seed(7)
+        for _ in shards:
+            w_up.append((torch.randn((H, d_s, args.up_project), generator=gen) / 16)
+                        .to(torch.bfloat16).cuda())
+        y_up = torch.empty((B, H, args.up_project), dtype=torch.float32, device="cuda")
+
     def step(r):
         tpla.rotate_append(q_raw, q_rot, new_raw, new_rope, new_seq, new_pos, caches[r], bt,
                            first_shard=shards[0], latent_norm=args.latent_norm)
         for i, g in enumerate(shards):
             decode(r, i, g)
+        for i in range(len(w_up)):
+            tpla.up_project(outs[i], w_up[i], out=y_up, accumulate=i > 0)
 
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
@@ -358,7 +376,7 @@ def main():
                    "context": (list(cfg.ctx) if isinstance(cfg.ctx, tuple) else cfg.ctx),
                    "tokens_attended": lens_sum, "block_size": cfg.block_size,
                    "cache_replicas": replicas, "global_batch": B, "num_splits": splits,
-                   "latent_norm": args.latent_norm,
+                   "latent_norm": args.latent_norm, "up_project_d_v": args.up_project,
                    "seq_len": maxlen},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),

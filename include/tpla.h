@@ -320,7 +320,7 @@ tpla_status tpla_decode_shard(const tpla_decode_args* args, void* workspace,
  *  y   device, element (b, h, v) at y + b*y_stride_b + h*y_stride_h + v;
  *      must not overlap o or w.
  *  dtypes  TPLA_FP32 or TPLA_BF16 each.  Products and sums in float32 (the
- *      k range split in four parts added in a fixed order); one rounding to
+ *      k range split in sixteen parts added in a fixed order); one rounding to
  *      y's type, after the addition of the old value when accumulating.
  * Requirements: batch, heads, d_s, d_v >= 1; d_s <= 1024; heads <= 65535;
  * o_stride_h >= d_s, w_stride_k >= d_v, w_stride_h >= d_s * w_stride_k,
