@@ -249,13 +249,13 @@ def main():
                           cfg.scale, maxlen, out=outs[i], lse=lses[i], num_splits=splits,
                           workspace=workspace)
 
-    # optional value up-projection: each shard's rows of every head's
-    # transposed W_UV (synthetic, seeded), the shards' terms summed into y
+    # optional value up-projection: each shard's latent columns of every
+    # head's W_UV (synthetic, seeded), the shards' terms summed into y
     w_up, y_up = [], None
     if args.up_project:
         gen = torch.Generator(device="cpu").manual_seed(7)
         for _ in shards:
-            w_up.append((torch.randn((H, d_s, args.up_project), generator=gen) / 16)
+            w_up.append((torch.randn((H, args.up_project, d_s), generator=gen) / 16)
                         .to(torch.bfloat16).cuda())
         y_up = torch.empty((B, H, args.up_project), dtype=torch.float32, device="cuda")
 

@@ -302,35 +302,35 @@ tpla_status tpla_decode_shard(const tpla_decode_args* args, void* workspace,
 /*
  * tpla_up_project: one device's value up-projection, optionally added into
  * an output that already holds other devices' terms:
- *     y[b, h, v] = (accumulate ? y[b, h, v] : 0) + sum_k o[b, h, k] * w[h, k, v]
+ *     y[b, h, v] = (accumulate ? y[b, h, v] : 0) + sum_k o[b, h, k] * w[h, v, k]
  * for b < batch, h < heads, v < d_v, k < d_s.
  *
  * Under TPLA a device's attention output o covers only its latent slice;
- * the head's output is the sum over devices of o times the matching rows of
- * the head's W_UV, and that sum is the all-reduce (TPLA abstract: per-shard
+ * the head's output is the sum over devices of W_UV's matching columns
+ * times o, and that sum is the all-reduce (TPLA abstract: per-shard
  * attention combined with an all-reduce; paperbot revised abstract: the
- * orthogonal reparameterisation keeps MLA's weights usable).  w holds the
- * device's rows of every head's W_UV transposed (latent index first); with
- * a rotated latent (tpla_hadamard_latent) they are the rows of Hn @ W_UV^T.
- * On one device the all-reduce is the accumulation of the devices' calls
- * into one y.
+ * orthogonal reparameterisation keeps MLA's weights usable).  w is W_UV in
+ * its own layout ([head][v][latent]) restricted to the device's latent
+ * columns (w_stride_v = the full latent width for a column slice); with a
+ * rotated latent (tpla_hadamard_latent) it is W_UV . Hn.  On one device the
+ * all-reduce is the accumulation of the devices' calls into one y.
  *
  *  o   device, element (b, h, k) at o + b*o_stride_b + h*o_stride_h + k.
- *  w   device, element (h, k, v) at w + h*w_stride_h + k*w_stride_k + v.
+ *  w   device, element (h, v, k) at w + h*w_stride_h + v*w_stride_v + k.
  *  y   device, element (b, h, v) at y + b*y_stride_b + h*y_stride_h + v;
  *      must not overlap o or w.
- *  dtypes  TPLA_FP32 or TPLA_BF16 each.  Products and sums in float32 (the
- *      k range split in sixteen parts added in a fixed order); one rounding to
- *      y's type, after the addition of the old value when accumulating.
- * Requirements: batch, heads, d_s, d_v >= 1; d_s <= 1024; heads <= 65535;
- * o_stride_h >= d_s, w_stride_k >= d_v, w_stride_h >= d_s * w_stride_k,
- * y_stride_h >= d_v, batch strides >= 0.
- * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE, TPLA_ERR_DTYPE, TPLA_ERR_UNSUPPORTED
- * (d_s > 1024), TPLA_ERR_HIP.
+ *  dtypes  TPLA_FP32 or TPLA_BF16 each.  The products are exact (float32
+ *      operands are split into three bf16 terms on the matrix cores) and
+ *      summed in float32; one rounding to y's type, after the addition of
+ *      the old value when accumulating.
+ * Requirements: batch, heads, d_s, d_v >= 1; heads <= 65535; batch <=
+ * 2097120; o_stride_h >= d_s, w_stride_v >= d_s, w_stride_h >= d_v *
+ * w_stride_v, y_stride_h >= d_v, batch strides >= 0.
+ * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE, TPLA_ERR_DTYPE, TPLA_ERR_HIP.
  */
 tpla_status tpla_up_project(const void* o, tpla_dtype o_dtype, int64_t o_stride_b,
                             int64_t o_stride_h, const void* w, tpla_dtype w_dtype,
-                            int64_t w_stride_h, int64_t w_stride_k, void* y, tpla_dtype y_dtype,
+                            int64_t w_stride_h, int64_t w_stride_v, void* y, tpla_dtype y_dtype,
                             int64_t y_stride_b, int64_t y_stride_h, int32_t batch, int32_t heads,
                             int32_t d_s, int32_t d_v, int32_t accumulate, void* stream);
 

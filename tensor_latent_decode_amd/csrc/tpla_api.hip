@@ -459,7 +459,7 @@ tpla_status tpla_decode_shard(const tpla_decode_args* a, void* workspace, size_t
 
 tpla_status tpla_up_project(const void* o, tpla_dtype o_dtype, int64_t o_stride_b,
                             int64_t o_stride_h, const void* w, tpla_dtype w_dtype,
-                            int64_t w_stride_h, int64_t w_stride_k, void* y, tpla_dtype y_dtype,
+                            int64_t w_stride_h, int64_t w_stride_v, void* y, tpla_dtype y_dtype,
                             int64_t y_stride_b, int64_t y_stride_h, int32_t batch, int32_t heads,
                             int32_t d_s, int32_t d_v, int32_t accumulate, void* stream) {
   if (!valid_dtype(o_dtype) || !valid_dtype(w_dtype) || !valid_dtype(y_dtype))
@@ -467,11 +467,10 @@ tpla_status tpla_up_project(const void* o, tpla_dtype o_dtype, int64_t o_stride_
   if (batch < 1 || heads < 1 || d_s < 1 || d_v < 1)
     return fail(TPLA_ERR_SHAPE, "batch, heads, d_s, d_v must be >= 1");
   if (heads > 65535) return fail(TPLA_ERR_SHAPE, "heads=%d exceeds 65535", heads);
-  if (o_stride_h < d_s || w_stride_k < d_v || w_stride_h < static_cast<int64_t>(d_s) * w_stride_k ||
+  if (batch > 65535 * 32) return fail(TPLA_ERR_SHAPE, "batch=%d exceeds %d", batch, 65535 * 32);
+  if (o_stride_h < d_s || w_stride_v < d_s || w_stride_h < static_cast<int64_t>(d_v) * w_stride_v ||
       y_stride_h < d_v || o_stride_b < 0 || y_stride_b < 0)
     return fail(TPLA_ERR_SHAPE, "strides must cover a row");
-  if (d_s > tpla::kMaxUpProjectK)
-    return fail(TPLA_ERR_UNSUPPORTED, "d_s=%d exceeds %d", d_s, tpla::kMaxUpProjectK);
   if (o == nullptr || w == nullptr || y == nullptr) return fail(TPLA_ERR_NULL, "o, w and y are required");
   tpla::UpProjectParams p{};
   p.o = o;
@@ -479,7 +478,7 @@ tpla_status tpla_up_project(const void* o, tpla_dtype o_dtype, int64_t o_stride_
   p.o_sh = o_stride_h;
   p.w = w;
   p.w_sh = w_stride_h;
-  p.w_sk = w_stride_k;
+  p.w_sv = w_stride_v;
   p.y = y;
   p.y_sb = y_stride_b;
   p.y_sh = y_stride_h;

@@ -112,13 +112,12 @@ struct RotateAppendParams {
   float norm_eps;
 };
 
-// Value up-projection: y[b, h, v] (+)= sum_k o[b, h, k] * w[h, k, v].
-constexpr int kMaxUpProjectK = 1024;   // d_s limit (the head's rows of o are staged in LDS)
+// Value up-projection: y[b, h, v] (+)= sum_k o[b, h, k] * w[h, v, k].
 struct UpProjectParams {
   const void* o;
   int64_t o_sb, o_sh;
   const void* w;
-  int64_t w_sh, w_sk;
+  int64_t w_sh, w_sv;
   void* y;
   int64_t y_sb, y_sh;
   int batch, heads, d_s, d_v;

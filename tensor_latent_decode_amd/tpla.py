@@ -290,16 +290,17 @@ def rotate_append(q: Optional[torch.Tensor], q_out: Optional[torch.Tensor],
 
 def up_project(o: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,
                accumulate: bool = False, out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
-    """out[b, h, :] (+)= o[b, h, :] @ w[h] for o [B, H, d_s] and w [H, d_s, d_v]
-    (one device's rows of every head's transposed W_UV); accumulate=True adds
-    into `out`, which is how the shards' terms are summed on one device."""
+    """out[b, h, :] (+)= w[h] @ o[b, h, :] for o [B, H, d_s] and w [H, d_v, d_s]
+    (W_UV's columns of one device's latent slice; a column slice of the full
+    [H, d_v, d_c] weight is fine); accumulate=True adds into `out`, which is
+    how the shards' terms are summed on one device."""
     _gpu(o, w, out)
     if o.dim() != 3 or w.dim() != 3 or o.stride(-1) != 1 or w.stride(-1) != 1:
-        raise ValueError("o must be [B, H, d_s] and w [H, d_s, d_v] with contiguous last dims")
+        raise ValueError("o must be [B, H, d_s] and w [H, d_v, d_s] with contiguous last dims")
     B, H, d_s = o.shape
-    if w.shape[0] != H or w.shape[1] != d_s:
-        raise ValueError("w must be [H, d_s, d_v] matching o")
-    d_v = w.shape[2]
+    if w.shape[0] != H or w.shape[2] != d_s:
+        raise ValueError("w must be [H, d_v, d_s] matching o")
+    d_v = w.shape[1]
     if out is None:
         if accumulate:
             raise ValueError("accumulate needs out")

@@ -209,11 +209,11 @@ def test_suggest_splits_argument_checks():
 
 def test_up_project_argument_checks():
     L = tpla.lib()
-    base = [FAKE, 1, 128 * 256, 256, FAKE, 1, 256 * 128, 128, FAKE, 0, 128 * 128, 128,
+    base = [FAKE, 1, 128 * 256, 256, FAKE, 1, 128 * 512, 512, FAKE, 0, 128 * 128, 128,
             16, 128, 256, 128, 0, None]
     def call(**kw):
         args = list(base)
-        names = ["o", "o_dt", "o_sb", "o_sh", "w", "w_dt", "w_sh", "w_sk", "y", "y_dt", "y_sb",
+        names = ["o", "o_dt", "o_sb", "o_sh", "w", "w_dt", "w_sh", "w_sv", "y", "y_dt", "y_sb",
                  "y_sh", "batch", "heads", "d_s", "d_v", "acc", "stream"]
         for k, v in kw.items():
             args[names.index(k)] = v
@@ -222,13 +222,13 @@ def test_up_project_argument_checks():
     _fails(call(y_dt=7), 4)
     _fails(call(batch=0), 2)
     _fails(call(d_v=0), 2)
-    _fails(call(heads=70000, w_sh=256 * 128), 2)
+    _fails(call(heads=70000), 2)
+    _fails(call(batch=65535 * 32 + 1), 2)
     _fails(call(o_sh=100), 2)                  # head stride shorter than d_s
-    _fails(call(w_sk=64), 2)                   # row stride shorter than d_v
-    _fails(call(w_sh=1000), 2)                 # head stride shorter than d_s rows
+    _fails(call(w_sv=200), 2)                  # row stride shorter than d_s
+    _fails(call(w_sh=1000), 2)                 # head stride shorter than d_v rows
     _fails(call(y_sh=64), 2)
     _fails(call(o_sb=-1), 2)
-    _fails(call(d_s=2048, o_sh=2048, w_sh=2048 * 128), 5)
     _fails(call(o=None), 1)
     _fails(call(w=None), 1)
     _fails(call(y=None), 1)

@@ -625,19 +625,20 @@ def test_ragged_tp2_full_step_sampled():
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("B,H,d_s,d_v", [(16, 128, 256, 128), (20, 8, 200, 100), (1, 3, 1024, 70),
-                                         (33, 2, 64, 257)])
+                                         (33, 2, 64, 257), (5, 4, 37, 33), (40, 2, 12, 8)])
 @pytest.mark.parametrize("dts", [("f32", "bf16", "f32"), ("bf16", "bf16", "bf16"), ("f32", "f32", "f32")])
 def test_up_project_parity(B, H, d_s, d_v, dts):
-    # several batch passes (B > 16), partial column blocks, d_s not a
-    # multiple of four, strided o (a column slice of a wider output)
+    # several batch tiles (B > 32), partial row tiles of v, d_s with a partial
+    # k-step or not a multiple of 8 (element reads), o misaligned (a column
+    # slice of a wider output) or contiguous (16-byte reads)
     rng = np.random.default_rng(B * 1000 + d_s)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
     wide = torch.from_numpy(rng.standard_normal((B, H, d_s + 7)).astype(np.float32)).cuda()
     o = wide[:, :, 3:3 + d_s].to(tdt[dts[0]]) if dts[0] == "bf16" else wide[:, :, 3:3 + d_s]
-    w = torch.from_numpy((rng.standard_normal((H, d_s, d_v)) / 16).astype(np.float32)).cuda().to(tdt[dts[1]])
+    w = torch.from_numpy((rng.standard_normal((H, d_v, d_s)) / 16).astype(np.float32)).cuda().to(tdt[dts[1]])
     y = tpla.up_project(o, w, out_dtype=tdt[dts[2]])
     torch.cuda.synchronize()
-    ref = oracle.up_project_shard(host_f64(o), host_f64(w))
+    ref = oracle.up_project_shard(host_f64(o), host_f64(w).transpose(0, 2, 1))
     tol = TOL_BF16 if dts[2] == "bf16" else TOL_FP32
     assert rel_err(host_f64(y), ref) <= tol
 
@@ -647,13 +648,13 @@ def test_up_project_accumulates_shards():
     rng = np.random.default_rng(5)
     B, H, d_s, d_v, T = 16, 16, 256, 128, 2
     os_ = [torch.from_numpy(rng.standard_normal((B, H, d_s)).astype(np.float32)).cuda() for _ in range(T)]
-    ws = [torch.from_numpy((rng.standard_normal((H, d_s, d_v)) / 16).astype(np.float32)).cuda()
+    ws = [torch.from_numpy((rng.standard_normal((H, d_v, d_s)) / 16).astype(np.float32)).cuda()
           .to(torch.bfloat16) for _ in range(T)]
     y = tpla.up_project(os_[0], ws[0])
     tpla.up_project(os_[1], ws[1], out=y, accumulate=True)
     y1 = tpla.up_project(os_[1], ws[1])
     torch.cuda.synchronize()
-    ref = oracle.up_project_combine([host_f64(o) for o in os_], [host_f64(w) for w in ws])
+    ref = oracle.up_project_combine([host_f64(o) for o in os_], [host_f64(w).transpose(0, 2, 1) for w in ws])
     assert rel_err(host_f64(y), ref) <= TOL_FP32
     # the second call added its own result to the first one's, in float32
     y0 = tpla.up_project(os_[0], ws[0])
@@ -672,18 +673,32 @@ def test_full_step_with_up_projection(hadamard):
     d_s, d_v = cfg.d_s, 128
     rng = np.random.default_rng(89)
     w_t = rng.standard_normal((cfg.heads, cfg.d_c, d_v)) / 16          # [H, d_c, d_v]
-    w_dev = np.ascontiguousarray(oracle.rotate_weight_rows(w_t) if hadamard else w_t)
+    w_dev = oracle.rotate_weight_rows(w_t) if hadamard else w_t
+    w_dev = np.ascontiguousarray(w_dev.transpose(0, 2, 1))          # W_UV layout [H, d_v, d_c]
     _, outs, _ = run_step(gc, hadamard)
     w_gpu = torch.from_numpy(w_dev.astype(np.float32)).cuda().to(torch.bfloat16)
     y = None
     for g in range(cfg.tp):
-        wg = w_gpu[:, g * d_s:(g + 1) * d_s, :]
+        wg = w_gpu[:, :, g * d_s:(g + 1) * d_s]                     # column slice
         y = tpla.up_project(outs[g], wg, out=y, accumulate=g > 0)
     torch.cuda.synchronize()
-    w_used = host_f64(w_gpu)           # the bf16 weights as the kernel saw them
+    w_used = host_f64(w_gpu).transpose(0, 2, 1)    # bf16 weights as the kernel saw them, [H, d_c, d_v]
     for b in range(cfg.batch):
         _, parts = oracle_step(case, b, cfg.tp, hadamard=hadamard)
         o_sh = [p[0][None] for p in parts]
         w_sh = [w_used[:, g * d_s:(g + 1) * d_s, :] for g in range(cfg.tp)]
         ref = oracle.up_project_combine(o_sh, w_sh)[0]
         assert rel_err(host_f64(y)[b], ref) <= TOL_BF16, b
+
+
+@pytest.mark.parametrize("d_s", [100, 12, 264])
+def test_up_project_aligned_float32_partial_kstep(d_s):
+    # contiguous float32 o and w with d_s % 8 == 4: 16-byte reads whose last
+    # window is shifted back into the row
+    rng = np.random.default_rng(d_s)
+    o = torch.from_numpy(rng.standard_normal((9, 3, d_s)).astype(np.float32)).cuda()
+    w = torch.from_numpy(rng.standard_normal((3, 40, d_s)).astype(np.float32)).cuda()
+    y = tpla.up_project(o, w)
+    torch.cuda.synchronize()
+    ref = oracle.up_project_shard(host_f64(o), host_f64(w).transpose(0, 2, 1))
+    assert rel_err(host_f64(y), ref) <= TOL_FP32
