@@ -16,7 +16,10 @@ RMS norm of the new latent to the append.
 The default workload is the DeepSeek-V3-shaped shard at 32K context
 (B=16, H=128, d_c=512 split TP=2 -> d_s=256, d_r=64, paged blocks of 64 with
 a permuted block table); `--workload ragged_tp2` runs both shards of the
-ragged TP=2 step in turn.
+ragged TP=2 step in turn.  `--workload mla_tp2_32k` is the comparison TPLA
+is measured against: plain MLA under TP=2, one device's 64 of the 128 heads
+over the whole 512-wide latent (no rotation: the step appends the new row
+with tpla_append_kv and decodes).
 
 Steps are replayed from HIP graphs (one holding several steps, cache replicas
 in turn, plus one per replica for a remainder).  Replicas rotate
@@ -61,7 +64,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv3_32k",
-                    choices=["dsv3_32k", "kimi_k2_32k", "ragged_tp2", "dsv3_4k"])
+                    choices=["dsv3_32k", "kimi_k2_32k", "ragged_tp2", "dsv3_4k", "mla_tp2_32k"])
     ap.add_argument("--mode", default="step", choices=["step", "decode", "copy"])
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = auto)")
     ap.add_argument("--num-splits", type=int, default=0)
@@ -131,6 +134,7 @@ def cpu_baseline(case, seconds: float):
     cfg = case.cfg
     d_s, tp = cfg.d_s, cfg.tp
     shards = list(range(tp)) if cfg.name == "ragged_tp2" else [0]
+    rotate = tp > 1             # plain MLA (one shard) has no rotation
     bs = cfg.block_size
     f64 = oracle.bf16_bits_to_f64
     starts = np.concatenate([[0], np.cumsum(case.seq_lens - 1)])
@@ -149,8 +153,12 @@ def cpu_baseline(case, seconds: float):
                                 case.hist_rope[rows])
             caches.append(cache)
         t0 = time.perf_counter()
-        q = oracle.fwht(f64(case.q_latent[b]))
-        new = oracle.f32_to_bf16_bits(oracle.fwht(f64(case.new_latent[b])[None]).astype(np.float32))
+        q = f64(case.q_latent[b])
+        new = f64(case.new_latent[b])[None]
+        if rotate:
+            q = oracle.fwht(q)
+            new = oracle.fwht(new)
+        new = oracle.f32_to_bf16_bits(new.astype(np.float32))
         outs = []
         for g, cache in zip(shards, caches):
             oracle.paged_append(cache, case.block_table, bs, np.array([b]), case.new_pos[b:b + 1],
@@ -168,8 +176,8 @@ def cpu_baseline(case, seconds: float):
     return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{done_seqs} of {cfg.batch} sequences of the same workload (whole step "
-                      f"per sequence: rotate, append, paged gather + fp64 attention per shard, "
-                      f"combine), {elapsed:.1f} s on the host; tokens/s "
+                      f"per sequence: {'rotate, ' if rotate else ''}append, paged gather + fp64 "
+                      f"attention per shard, combine), {elapsed:.1f} s on the host; tokens/s "
                       f"{done_seqs / elapsed:.3g}"}
 
 
@@ -201,6 +209,10 @@ def main():
     cfg = case.cfg
     B, H, d_c, d_s, d_r, tp = cfg.batch, cfg.heads, cfg.d_c, cfg.d_s, cfg.d_r, cfg.tp
     shards = list(range(tp)) if args.workload == "ragged_tp2" else [0]
+    rotate = tp > 1             # plain MLA (one shard) has no rotation
+    if not rotate and args.latent_norm != "none":
+        print("--latent-norm applies to the rotated TPLA workloads only", file=sys.stderr)
+        sys.exit(2)
 
     def dev(a):
         if a.dtype == np.uint16:
@@ -228,7 +240,7 @@ def main():
         caches.append(per)
     del hist_lat, hist_rope, hist_seq, hist_pos
     maxlen = int(case.seq_lens.max())
-    q_rot = torch.empty((B, H, d_c), dtype=torch.bfloat16, device="cuda")
+    q_rot = torch.empty((B, H, d_c), dtype=torch.bfloat16, device="cuda") if rotate else q_raw
     # the combine: shard i's merge writes its latent columns of the combined
     # output directly (placement of disjoint slices; tpla_combine_shards does
     # the same for outputs held in separate buffers)
@@ -260,8 +272,11 @@ def main():
         y_up = torch.empty((B, H, args.up_project), dtype=torch.float32, device="cuda")
 
     def step(r):
-        tpla.rotate_append(q_raw, q_rot, new_raw, new_rope, new_seq, new_pos, caches[r], bt,
-                           first_shard=shards[0], latent_norm=args.latent_norm)
+        if rotate:
+            tpla.rotate_append(q_raw, q_rot, new_raw, new_rope, new_seq, new_pos, caches[r], bt,
+                               first_shard=shards[0], latent_norm=args.latent_norm)
+        else:
+            tpla.append_kv(caches[r][0], bt, new_seq, new_pos, new_raw, new_rope)
         for i, g in enumerate(shards):
             decode(r, i, g)
         for i in range(len(w_up)):

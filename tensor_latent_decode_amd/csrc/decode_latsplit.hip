@@ -631,25 +631,32 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
 
 }  // namespace
 
-int decode_latsplit_max_chunk() { return kMaxTiles * kTile; }
+int decode_latsplit_max_chunk() { return min(kMaxTiles * kTile, decode_mla_max_chunk()); }
 
 int decode_latsplit_partial_block() { return 64; }
 
 // Instantiations: 128-head groups with d_s = 256 (four waves, three K
 // buffers, one workgroup per CU) and 64-head groups with d_s = 128 (two
 // waves, two K buffers, two workgroups per CU); both with d_r = 64.
+// The 512-wide latent (plain MLA under tensor parallelism, or a one-shard
+// TPLA) goes to the kernel in decode_mla.hip, which keeps the same split
+// output format.
 bool decode_latsplit_supported(int heads, int d_s, int d_r, int block_size) {
+  if (decode_mla_supported(heads, d_s, d_r, block_size)) return true;
   if (block_size % kTile != 0 || d_r != 64) return false;
   if (heads % 128 == 0 && d_s == 256) return true;
   return heads % 64 == 0 && d_s == 128;
 }
 
-int decode_latsplit_groups_per_cu(int heads, int d_s) { return (heads % 128 == 0 && d_s == 256) ? 1 : 2; }
+int decode_latsplit_groups_per_cu(int heads, int d_s) {
+  return ((heads % 128 == 0 && d_s == 256) || d_s == 512) ? 1 : 2;
+}
 
 int decode_latsplit_heads_per_group(int heads, int d_s) { return (heads % 128 == 0 && d_s == 256) ? 128 : 64; }
 
 hipError_t launch_decode_latsplit(const DecodeParams& p, hipStream_t s) {
   if (!decode_latsplit_supported(p.heads, p.d_s, p.d_r, p.block_size)) return hipErrorNotSupported;
+  if (decode_mla_supported(p.heads, p.d_s, p.d_r, p.block_size)) return launch_decode_mla(p, s);
   if (p.heads % 128 == 0 && p.d_s == 256) return launch_t<4, 256, 64, 3>(p, s);
   return launch_t<2, 128, 64, 2>(p, s);
 }

@@ -139,11 +139,12 @@ tpla_status plan_decode(const tpla_decode_args* a, Plan* pl) {
     int64_t groups = a->batch;
     int per_cu = 2;
     const Path path = decode_path(a);
-    if (path != Path::kGeneric) {
+    if (path == Path::kStream) {
+      groups *= a->heads / tpla::decode_latsplit_heads_per_group(a->heads, a->d_s);
+      per_cu = tpla::decode_latsplit_groups_per_cu(a->heads, a->d_s);
+    } else if (path == Path::kMfma) {
       groups *= a->heads / (32 * (a->heads % 128 == 0 ? 4 : (a->heads % 64 == 0 ? 2 : 1)));
-      per_cu = path == Path::kStream
-                   ? tpla::decode_latsplit_groups_per_cu(a->heads, a->d_s)
-                   : tpla::decode_mfma_groups_per_cu(a->heads, a->d_s, a->d_r);
+      per_cu = tpla::decode_mfma_groups_per_cu(a->heads, a->d_s, a->d_r);
     } else {
       groups *= (a->heads + 7) / 8;
     }

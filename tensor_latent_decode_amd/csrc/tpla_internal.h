@@ -145,6 +145,9 @@ int decode_latsplit_groups_per_cu(int heads, int d_s);   // workgroups per CU th
 int decode_latsplit_heads_per_group(int heads, int d_s);
 int decode_latsplit_max_chunk();   // tokens per split the latent-split kernel accepts
 int decode_latsplit_partial_block();   // columns per scale of its fp16 split outputs
+hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t s);
+bool decode_mla_supported(int heads, int d_s, int d_r, int block_size);
+int decode_mla_max_chunk();
 hipError_t launch_decode_generic(const DecodeParams& p, int is_bf16, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_combine(const PartPtrs& parts, int part_bf16, int tp, int batch, int heads,

@@ -16,7 +16,7 @@ import oracle
 from tensor_latent_decode_amd import tpla
 from tensor_latent_decode_amd.inputs import CONFIGS, make_case
 from tpla_testlib import (TOL_BF16, TOL_FP32, GpuCase, as_f64, dev, host_bits, host_f64,
-                          oracle_step, rel_err)
+                          oracle_rows, oracle_step, rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -398,6 +398,8 @@ SHAPES = [  # (heads, d_c, tp, d_r)
     (64, 512, 4, 64),       # Kimi-K2 shard
     (32, 128, 2, 64),
     (128, 256, 2, 0),
+    (64, 512, 1, 64),       # plain MLA under TP=2: 64 heads, whole latent
+    (128, 512, 1, 64),      # plain MLA, one device
 ]
 
 
@@ -411,6 +413,12 @@ def test_decode_bf16_ragged_parity(shape, bs, splits):
     cfg = replace(cfg, heads=H, d_c=d_c, tp=tp, d_r=d_r, scale=1 / math.sqrt(192.0))
     case = make_case(cfg, batch=6, ctx=(1, 700), block_size=bs, seed=31 + H + bs)
     gc = GpuCase(case)
+    if d_c // tp == 512 and bs % 32 != 0:
+        # the 512-wide kernel copies 32-token runs of one block; nothing else
+        # takes a 512-wide latent in bf16
+        with pytest.raises(tpla.TplaError, match="(?i)unsupported"):
+            run_step(gc, hadamard=False, num_splits=splits)
+        return
     combined, outs, lses = run_step(gc, hadamard=False, num_splits=splits)
     got = host_f64(combined)
     for b in range(cfg.batch):
@@ -420,8 +428,8 @@ def test_decode_bf16_ragged_parity(shape, bs, splits):
             assert np.max(np.abs(host_f64(lses[g])[b] - l)) <= 2e-2
 
 
-@pytest.mark.parametrize("shape", SHAPES[:3])
-@pytest.mark.parametrize("bs", [64, 16])
+@pytest.mark.parametrize("shape,bs", [(sh, bs) for sh in SHAPES[:3] for bs in (64, 16)] +
+                         [(SHAPES[4], 64), (SHAPES[4], 32)])
 def test_decode_bf16_late_score_spike(shape, bs):
     """A token deep inside the first split scores far above everything before
     it (head 0: about 2500 raw, ~260 in base-2 exponent units), so a softmax
@@ -535,10 +543,84 @@ def test_decode_bf16_output_and_determinism():
 
 
 # --------------------------------------------------------------------------
+# Plain MLA under tensor parallelism (whole 512-wide latent, 64-head groups)
+# --------------------------------------------------------------------------
+
+def mla_case(heads=64, batch=3, ctx=(1, 900), bs=64, seed=80, scale=None):
+    from dataclasses import replace
+    cfg = CONFIGS["mla_tp2_32k"]
+    cfg = replace(cfg, heads=heads, scale=cfg.scale if scale is None else scale)
+    return make_case(cfg, batch=batch, ctx=ctx, block_size=bs, seed=seed)
+
+
+def mla_decode(gc: GpuCase, lens=None, **kw):
+    case = gc.case
+    cache = gc.prefill(0, 512)
+    lens = gc.hist_lens if lens is None else lens
+    lse = torch.empty((case.cfg.batch, case.cfg.heads), dtype=torch.float32, device="cuda")
+    o, _ = tpla.decode_shard(gc.q_latent, gc.q_rope, cache, gc.bt, lens, case.cfg.scale,
+                             int(case.seq_lens.max()), lse=lse, **kw)
+    torch.cuda.synchronize()
+    return host_f64(o), host_f64(lse)
+
+
+def mla_reference(case, b: int, n: int):
+    """The oracle's plain MLA decode over the first n history rows of sequence b."""
+    lat, rope = oracle_rows(case, b)
+    return oracle.mla_decode(as_f64(case.q_latent[b]), as_f64(case.q_rope[b]), lat[:n], rope[:n],
+                             case.cfg.scale)
+
+
+@pytest.mark.parametrize("scale", [-0.07, 0.0, 0.3])
+def test_mla_decode_any_scale(scale):
+    """Zero and negative scales are valid softmax scales (a zero scale is the
+    plain mean of the rows)."""
+    case = mla_case(batch=2, ctx=(200, 700), seed=81, scale=scale)
+    gc = GpuCase(case)
+    o, lse = mla_decode(gc, num_splits=2)
+    for b in range(2):
+        n = int(case.seq_lens[b]) - 1
+        ref_o, ref_l = mla_reference(case, b, n)
+        assert rel_err(o[b], ref_o) <= TOL_BF16, b
+        assert np.max(np.abs(lse[b] - ref_l)) <= 2e-2
+
+
+@pytest.mark.parametrize("lens", [[1, 31, 32, 33], [63, 64, 65, 95], [96, 97, 2047, 2049]])
+def test_mla_decode_tile_edges(lens):
+    """Lengths at and around the 32-token tile and the 64-token block."""
+    case = mla_case(heads=128, batch=4, ctx=max(lens) + 1, seed=82)
+    gc = GpuCase(case)
+    L = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    for splits in (0, 1, 5):
+        o, lse = mla_decode(gc, lens=L, num_splits=splits)
+        for b, n in enumerate(lens):
+            ref_o, ref_l = mla_reference(case, b, n)
+            assert rel_err(o[b], ref_o) <= TOL_BF16, (splits, b, n)
+            assert np.max(np.abs(lse[b] - ref_l)) <= 2e-2, (splits, b, n)
+
+
+def test_mla_decode_deterministic_and_strided_query():
+    """Same bits on a second call; a query read through strides (heads of a
+    wider buffer) gives the same bits as a packed one."""
+    case = mla_case(batch=2, ctx=(900, 1500), seed=83)
+    gc = GpuCase(case)
+    a, _ = mla_decode(gc)
+    b, _ = mla_decode(gc)
+    assert np.array_equal(a, b)
+    wide = torch.zeros((2, 64, 640), dtype=torch.bfloat16, device="cuda")
+    wide[:, :, 64:576] = gc.q_latent
+    cache = gc.prefill(0, 512)
+    o, _ = tpla.decode_shard(wide[:, :, 64:576], gc.q_rope, cache, gc.bt, gc.hist_lens,
+                             case.cfg.scale, int(case.seq_lens.max()))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f64(o), a)
+
+
+# --------------------------------------------------------------------------
 # The workloads at their real sizes (sampled sequences)
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("heads,d_c,tp", [(128, 512, 2), (64, 512, 4)])
+@pytest.mark.parametrize("heads,d_c,tp", [(128, 512, 2), (64, 512, 4), (64, 512, 1)])
 def test_decode_split_longer_than_tile_table(heads, d_c, tp):
     """A single requested split longer than the streaming kernel's tile
     table (65536 tokens) is planned as more splits and stays exact."""
@@ -589,7 +671,7 @@ def test_dsv3_4k_full():
         assert rel_err(host_f64(outs[g])[0], parts[g][0]) <= TOL_BF16
 
 
-@pytest.mark.parametrize("name", ["dsv3_32k", "kimi_k2_32k"])
+@pytest.mark.parametrize("name", ["dsv3_32k", "kimi_k2_32k", "mla_tp2_32k"])
 def test_32k_shard_sampled(name):
     """One shard (g = 0) at its real shape, automatic splits as the bench runs it."""
     case = make_case(CONFIGS[name])
