@@ -20,16 +20,16 @@
 // run), so the split is about moving few bytes per MFMA:
 // * P^T fragments are exchanged through LDS (each wave writes its 32 heads,
 //   4 KiB per tile) and each fragment feeds MPW value MFMAs.
-// * V^T never goes through LDS.  The value A operand needs 8 consecutive
-//   tokens of one latent column per lane; the score A operand (K rows) is
-//   already in registers, and an MFMA with a 0/1 B operand moves it into
-//   the accumulator layout, which is exactly that fragment layout:
-//       D = K(ks=2m) . I_lo + K(ks=2m+1) . I_hi
-//   gives rows = tokens, columns = latent 32m .. 32m+31 (each output is one
-//   bf16 value times 1 plus exact zeros, so the round trip through fp32 and
-//   back to bf16 is exact for finite values).  Each wave transposes only its
-//   own MPW latent tiles; it visits their k-steps first (the k-step order is
-//   rotated per wave, and the query fragments are loaded in that order).
+// * V^T fragments come straight from the K tile by transposing LDS reads
+//   (ds_read_b64_tr_b16).  In each group of 16 lanes, lane j receives
+//   element j % 4 of the 8 bytes read by lanes 4k + j / 4, k = 0..3; lane
+//   4k + q reads token row t_k, latent columns 4q .. 4q+3 of the group's 16,
+//   so lane j gets four tokens of latent column j: half of a value A
+//   fragment (row = latent column, k = 8 tokens).  The tokens are taken in
+//   the order of the P^T fragments (16j + 8*(e/4) + 4h + e%4 for element e
+//   of fragment j in lane half h), so no other reordering is needed.  Each
+//   wave reads the fragments of its own MPW latent tiles while it scores the
+//   tile and keeps them for the next step's values.
 // * Tiles go from HBM straight into LDS (global_load_lds_dwordx4 from
 //   inline assembly, waited for explicitly: the compiler would otherwise
 //   wait for every copy in flight before each LDS read).  16-byte chunk c of
@@ -62,6 +62,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
 
 // Scalar (constant address space) read of a wave-uniform int32.
 __device__ __forceinline__ int scalar_load(const int32_t* p) { return *(const const_i32_t*)p; }
@@ -101,6 +104,11 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Transposing LDS read (lane layout in the header).
+__device__ __forceinline__ i16x4_t read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)((lds_char_t*)const_cast<char*>(p)));
+}
+
 __device__ __forceinline__ f32x16_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -129,7 +137,7 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   static_assert(CPR % 8 == 0 && DS % 64 == 0 && DR % 16 == 0, "shape");
   static_assert(MT % NW == 0 && MPW % 2 == 0, "latent tiles per wave");
   static_assert(((KL / 4) & (KL / 4 - 1)) == 0, "latent k-step groups must be a power of two");
-  static_assert(NPV <= 32 && kExpSlots <= NPV && KS > 2 * MPW, "schedule shape");
+  static_assert(NPV <= 32 && kExpSlots <= NPV && KS >= 4 * MPW, "schedule shape");
   // Tile copies: the first kCopyS ride on the score k-steps (one every
   // kCopyEveryS), any rest on the value MFMAs (one every kCopyEveryV).
   // Measured on the DeepSeek-V3 shard: all ten on the score k-steps is ~1-2%
@@ -219,8 +227,6 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;
   const int nfull = (t1 - t0) / kTile;
 
-  bf16x8_t ident[2];     // 0/1 B operands of the transposing MFMAs
-
   // ---- tile copies: chunk slot (i*NW + wave)*64 + lane of a tile ----
   uint32_t src_off[IPT];
 #pragma unroll
@@ -294,6 +300,30 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     return *reinterpret_cast<const bf16x8_t*>(T + qk_off[kk & 3] + mt * 32 * CPR * 16 + grp * 128);
   };
 
+  // Value A fragment (latent tile MPW*wave + mm, token k-step j) of the
+  // tile at T: two transposing reads, token rows 16j + 4h + k and
+  // 16j + 8 + 4h + k.  Byte offsets per (j, second read, latent tile odd).
+  uint32_t tr_off[4][2][2];
+  {
+    const int trk = (lane & 15) >> 2, trq = lane & 3, trg = (lane >> 4) & 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int row = 16 * j + 8 * rr + 4 * half + trk;
+#pragma unroll
+        for (int mo = 0; mo < 2; ++mo)
+          tr_off[j][rr][mo] = static_cast<uint32_t>(
+              row * CPR * 16 + ((4 * mo + 2 * trg + (trq >> 1)) ^ swz(row)) * 16 + 8 * (trq & 1));
+      }
+  }
+  auto rd_v = [&](const char* T, int mm, int j) -> bf16x8_t {
+    const char* b = T + 128 * ((MPW / 2) * wave + (mm >> 1));
+    const i16x4_t lo = read_tr(b + tr_off[j][0][mm & 1]);
+    const i16x4_t hi = read_tr(b + tr_off[j][1][mm & 1]);
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
   f32x16_t oacc[MPW][NW];    // O^T tiles: latent tile MPW*wave + mm, head tile ht
   bf16x8_t vc[MPW][4];       // V^T fragments of the tile whose values are due
   float m_run = -INFINITY;   // reference max of the scaled (base-2) scores
@@ -312,54 +342,19 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[mt][r] = 0.f;
-    // tacc[mm][mt]: transposition of latent tile mm, token rows 32*mt ..
-    f32x16_t tacc[MPW][2];
     bf16x8_t qa[4];
     qa[0] = rd_k(T, 0, 0);
     qa[1] = rd_k(T, 0, 1);
     qa[2] = rd_k(T, 1, 0);
     qa[3] = rd_k(T, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    // The fp32 -> bf16 conversion of the transposed tiles is spread over the
-    // later k-steps (one 8-value piece every other k-step from kCv0 on, or
-    // kPer pieces per k-step when there are few k-steps), so its register
-    // reads run in the shadow of the score MFMAs instead of waiting for the
-    // transposing MFMAs to finish.
-    constexpr int kPieces = MPW * 4;          // (mm, mt, hf)
-    constexpr int kStart = 2 * MPW + 1;       // one k-step after the last transposition
-    constexpr bool kSparse = KS - kStart >= 2 * kPieces - 1;
-    constexpr int kCv0 = kSparse ? KS - 2 * kPieces + 1 : kStart;
-    constexpr int kStride = kSparse ? 2 : 1;
-    constexpr int kPer = kSparse ? 1 : (kPieces + (KS - kStart) - 1) / (KS - kStart);
-    static_assert(kCv0 >= kStart && kCv0 + ((kPieces + kPer - 1) / kPer - 1) * kStride < KS,
-                  "conversions must fit after the last transposition");
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       sc[0] = mfma(qa[(2 * kk) & 3], qf[kk], sc[0]);
-      if (kk < 2 * MPW) {
-        const f32x16_t z = {};
-        tacc[kk >> 1][0] = mfma(qa[(2 * kk) & 3], ident[kk & 1], (kk & 1) ? tacc[kk >> 1][0] : z);
-      }
       if (kk + 2 < KS) qa[(2 * kk) & 3] = rd_k(T, kk + 2, 0);
       sc[1] = mfma(qa[(2 * kk + 1) & 3], qf[kk], sc[1]);
-      if (kk < 2 * MPW) {
-        const f32x16_t z = {};
-        tacc[kk >> 1][1] = mfma(qa[(2 * kk + 1) & 3], ident[kk & 1], (kk & 1) ? tacc[kk >> 1][1] : z);
-      }
       if (kk + 2 < KS) qa[(2 * kk + 1) & 3] = rd_k(T, kk + 2, 1);
-      if (kk >= kCv0 && (kk - kCv0) % kStride == 0) {
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-          // piece (mm, mt, hf): value A fragment for token k-step j = 2*mt + hf
-          const int pc = ((kk - kCv0) / kStride) * kPer + q;
-          if (pc < kPieces) {
-            const int mm = pc >> 2, mt = (pc >> 1) & 1, hf = pc & 1;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vt[mm][2 * mt + hf][e] = static_cast<__bf16>(tacc[mm][mt][8 * hf + e]);
-            asm volatile("" : "+v"(vt[mm][2 * mt + hf]));   // convert here, not at the loop latch
-          }
-        }
-      }
+      if (kk < 4 * MPW) vt[kk >> 2][kk & 3] = rd_v(T, kk >> 2, kk & 3);
       if (cj != nullptr && kk % kCopyEveryS == 0 && kk / kCopyEveryS < kCopyS)
         copy_chunk(*cj, kk / kCopyEveryS);
       __builtin_amdgcn_sched_barrier(0);
@@ -491,13 +486,6 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   // starts at the same time and the copies queue behind each other.)
 #pragma unroll
   for (int t = 0; t < 2; ++t) copy_all(make_job(t, t, t < ntiles ? tile_row(t, pg[t]) : 0u));
-  // 0/1 B operands: ident[0] picks k = j, ident[1] picks k = j - 16 for
-  // output column j (lane l holds column l % 32, k-slots 8*(l/32) ..).
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    ident[0][e] = static_cast<__bf16>((l31 == 8 * half + e) ? 1.0f : 0.0f);
-    ident[1][e] = static_cast<__bf16>((l31 == 16 + 8 * half + e) ? 1.0f : 0.0f);
-  }
   // Table of tile rows for the steps.
 #pragma unroll
   for (int k = 0; k < kFill; ++k) {
