@@ -19,7 +19,8 @@ a permuted block table); `--workload ragged_tp2` runs both shards of the
 ragged TP=2 step in turn.  `--workload mla_tp2_32k` is the comparison TPLA
 is measured against: plain MLA under TP=2, one device's 64 of the 128 heads
 over the whole 512-wide latent (no rotation: the step appends the new row
-with tpla_append_kv and decodes).
+with tpla_append_kv and decodes); `--workload mla_tp4_32k` is the same for
+Kimi-K2 under TP=4 (16 of its 64 heads per device).
 
 Steps are replayed from HIP graphs (one holding several steps, cache replicas
 in turn, plus one per replica for a remainder).  Replicas rotate
@@ -64,7 +65,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv3_32k",
-                    choices=["dsv3_32k", "kimi_k2_32k", "ragged_tp2", "dsv3_4k", "mla_tp2_32k"])
+                    choices=["dsv3_32k", "kimi_k2_32k", "ragged_tp2", "dsv3_4k", "mla_tp2_32k",
+                             "mla_tp4_32k"])
     ap.add_argument("--mode", default="step", choices=["step", "decode", "copy"])
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = auto)")
     ap.add_argument("--num-splits", type=int, default=0)

@@ -640,7 +640,10 @@ int decode_latsplit_groups_per_cu(int heads, int d_s) {
   return ((heads % 128 == 0 && d_s == 256) || d_s == 512) ? 1 : 2;
 }
 
-int decode_latsplit_heads_per_group(int heads, int d_s) { return (heads % 128 == 0 && d_s == 256) ? 128 : 64; }
+int decode_latsplit_heads_per_group(int heads, int d_s) {
+  if (d_s == 512) return decode_mla_group_heads(heads);
+  return (heads % 128 == 0 && d_s == 256) ? 128 : 64;
+}
 
 hipError_t launch_decode_latsplit(const DecodeParams& p, hipStream_t s) {
   if (!decode_latsplit_supported(p.heads, p.d_s, p.d_r, p.block_size)) return hipErrorNotSupported;

@@ -1,29 +1,31 @@
-// Streaming bf16 matrix-core split-K decode for 64-head groups over a
-// 512-wide latent with a 64-wide rope (gfx950): the shape of plain MLA
-// under tensor parallelism, where every device keeps the whole latent for
-// its share of the heads (TPLA abstract: under TP each device must load the
-// full cache; the comparison TPLA is measured against).  It is also a TPLA
-// "shard" at T = 1.
+// Streaming bf16 matrix-core split-K decode over a 512-wide latent with a
+// 64-wide rope (gfx950): the shape of plain MLA under tensor parallelism,
+// where every device keeps the whole latent for its share of the heads
+// (TPLA abstract: under TP each device must load the full cache; the
+// comparison TPLA is measured against).  It is also a TPLA "shard" at T = 1.
 //
-// One workgroup of four waves per (token split, sequence, group of 64
-// heads).  Tiles of 32 tokens (one contiguous run of 32 * 576 * 2 bytes
-// inside a page) go from HBM straight into LDS, three buffers deep.  Wave w
-// takes head tile w & 1 (32 heads) and latent half w >> 1 (256 columns and
-// 32 of the rope columns):
+// One workgroup of four waves per (token split, sequence, group of 64, 32
+// or 16 heads).  Tiles of 32 tokens (one contiguous run of 32 * 576 * 2
+// bytes inside a page) go from HBM straight into LDS, three buffers deep.
+// The group's NH head tiles of 32 (two for 64 heads, else one; a 16-head
+// group fills half a tile) and KP = 4 / NH parts of the latent give the
+// four waves: wave w takes head tile w % NH and latent part w / NH (512/KP
+// columns and 64/KP of the rope columns):
 //
-//   scores   a partial S^T[token, head] over the wave's 18 k-steps; the
-//            wave of the other half (same heads) adds its partial through
-//            LDS, so both hold the same full scores and the same softmax
-//   values   O^T[lat, head] += V^T . P^T for the wave's 256 latent columns
-//            and 32 heads, V^T made from the wave's own score A fragments
-//            by 0/1 MFMAs (exact for finite bf16 values)
+//   scores   a partial S^T[token, head] over the wave's k-steps; the waves
+//            of the other parts (same heads) add their partials through
+//            LDS in a fixed butterfly order, so all of them hold the same
+//            full scores and take the same softmax decisions
+//   values   O^T[lat, head] += V^T . P^T for the wave's latent columns and
+//            heads, V^T fragments straight from the K tile by transposing
+//            LDS reads (ds_read_b64_tr_b16, lane layout below)
 //
-// all on v_mfma_f32_32x32x16_bf16, 50 per wave per tile; P^T never leaves
-// the registers and one barrier per tile suffices.  The softmax runs against
-// a fixed reference (the split's first tile max); a later tile max more
-// than 64 (base 2) above it makes the split run again with the raised
-// reference.  Split outputs leave as fp16 with one float scale per (row, 64
-// columns), the format the split merge reads.
+// all on v_mfma_f32_32x32x16_bf16; P^T never leaves the registers and one
+// barrier per tile suffices.  The softmax runs against a fixed reference
+// (the split's first tile max); a later tile max more than 64 (base 2)
+// above it makes the split run again with the raised reference.  Split
+// outputs leave as fp16 with one float scale per (row, 64 columns), the
+// format the split merge reads.
 #include "tpla_internal.h"
 
 namespace tpla {
@@ -45,10 +47,9 @@ constexpr int kNT = 256;
 constexpr int kIPT = kSlots / kNT;     // copies per thread per tile (9)
 constexpr int kNB = 3;                 // K buffers
 constexpr int kMaxTiles = 2048;        // tiles per split (the host plans splits to fit)
-constexpr int kKW = 18;                // k-steps per wave: 16 latent + 2 rope
 constexpr float kRescale = 64.0f;
 constexpr float kLn2 = 0.69314718055994531f;
-static_assert(kSlots % kNT == 0 && 2 * kIPT == kKW, "one copy per two score k-steps");
+static_assert(kSlots % kNT == 0, "tile must split evenly over the workgroup");
 
 __device__ __forceinline__ int scalar_load(const int32_t* p) { return *(const const_i32_t*)p; }
 
@@ -104,8 +105,19 @@ __device__ __forceinline__ float both_halves_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// NH head tiles of 32 per workgroup (1 or 2); the latent is cut into
+// KP = 4 / NH parts, wave w = kp * NH + ht taking head tile ht and part kp.
+// hv: heads of a group that exist (16 for a 16-head group: lanes 16..31 of
+// the head tile repeat heads 0..15 and store nothing).
+template <int NH>
 __global__ __attribute__((amdgpu_flat_work_group_size(kNT, kNT), amdgpu_waves_per_eu(1, 1)))
-void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd) {
+void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd, int hv) {
+  constexpr int KP = 4 / NH;           // latent parts
+  constexpr int LK = 32 / KP;          // latent k-steps per part
+  constexpr int RK = 4 / KP;           // rope k-steps per part
+  constexpr int kKW = LK + RK;         // score k-steps per wave
+  constexpr int MTW = LK / 2;          // 32-column latent tiles per wave
+  static_assert(NH == 1 || NH == 2, "head tiles per group");
   __shared__ __attribute__((aligned(1024))) uint4 ktile[kNB][kSlots];
   __shared__ __attribute__((aligned(16))) float4 part[2][4][4][64];   // [tile & 1][wave][r/4][lane]
   __shared__ uint32_t trow[kMaxTiles];   // first cache row of each tile / 32
@@ -116,7 +128,7 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   const int u = (n & 7) * units_per_xcd + (n >> 3);
   if (u >= n_units) return;
   const int S = p.num_splits;
-  const int HG = p.heads / 64;
+  const int HG = p.heads / hv;
   const int split = u % S;
   const int bh = u / S;
   const int hg = bh % HG;
@@ -125,12 +137,13 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l31 = lane & 31, half = lane >> 5;
-  const int ht = wave & 1;      // head tile: heads head0 + 32*ht ..
-  const int kh = wave >> 1;     // latent half: columns 256*kh .. ; rope k-steps 2*kh, 2*kh+1
-  const int head0 = hg * 64;
-  const int hd = head0 + 32 * ht + l31;
+  const int ht = wave % NH;     // head tile: heads head0 + 32*ht ..
+  const int kh = wave / NH;     // latent part: columns 32*MTW*kh .. ; rope k-steps RK*kh ..
+  const int head0 = hg * hv;
+  const bool real = 32 * ht + l31 < hv;          // this lane's head exists
+  const int hd = head0 + (32 * ht + l31) % hv;
 
-  auto ks_of = [&](int j) -> int { return j < 16 ? 16 * kh + j : 32 + 2 * kh + (j - 16); };
+  auto ks_of = [&](int j) -> int { return j < LK ? LK * kh + j : 32 + RK * kh + (j - LK); };
 
   // First round trip: the block ids of the split's first two tiles, the
   // query fragments (B operand of S^T), the block ids of every tile for the
@@ -170,10 +183,7 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   const int t1 = min(L, t0 + p.chunk);
   const int64_t row0 = (static_cast<int64_t>(split) * p.batch + b) * p.heads;
   if (t0 >= t1) {
-    if (wave == 0 && half == 0) {
-      p.ws_lse[row0 + head0 + l31] = -INFINITY;
-      p.ws_lse[row0 + head0 + 32 + l31] = -INFINITY;
-    }
+    if (kh == 0 && half == 0 && real) p.ws_lse[row0 + hd] = -INFINITY;
     return;
   }
   const int ntiles = (t1 - t0 + kT - 1) / kT;
@@ -246,15 +256,15 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd) {
         tr_off[jj][rr][mo] = static_cast<uint32_t>(
             row * kCPR * 16 + ((4 * mo + 2 * trg + (trq >> 1)) ^ swz(row)) * 16 + 8 * (trq & 1));
     }
-  // fragment (m, jj) of latent tile 8*kh + m of the tile at T
+  // fragment (m, jj) of latent tile MTW*kh + m of the tile at T
   auto rd_v = [&](const char* T, int m, int jj) -> bf16x8_t {
-    const char* b = T + 128 * (4 * kh + (m >> 1));
+    const char* b = T + 128 * ((MTW / 2) * kh + (m >> 1));
     const i16x4_t lo = read_tr(b + tr_off[jj][0][m & 1]);
     const i16x4_t hi = read_tr(b + tr_off[jj][1][m & 1]);
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  f32x16_t oacc[8];      // O^T tiles: latent tile 8*kh + m, this wave's heads
+  f32x16_t oacc[MTW];    // O^T tiles: latent tile MTW*kh + m, this wave's heads
   float m_run = -INFINITY;   // reference max of this lane's head (scaled, base 2)
   float l_part;          // this lane's share of its head's row sum
   float m_seen;
@@ -266,7 +276,7 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   auto tile = [&](int i, bool first) {
     const char* T = reinterpret_cast<const char*>(&ktile[i % kNB][0]);
     f32x16_t sp = {};
-    bf16x8_t vf[8][2];
+    bf16x8_t vf[MTW][2];
     bf16x8_t kf[3];
     kf[0] = rd_k(T, ks_of(0));
     kf[1] = rd_k(T, ks_of(1));
@@ -275,7 +285,7 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     for (int j = 0; j < kKW; ++j) {
       const bf16x8_t a = kf[j % 3];
       if (j + 2 < kKW) kf[(j + 2) % 3] = rd_k(T, ks_of(j + 2));
-      if (j < 16) vf[j >> 1][j & 1] = rd_v(T, j >> 1, j & 1);
+      if (j < LK) vf[j >> 1][j & 1] = rd_v(T, j >> 1, j & 1);
       sp = mfma(a, qf[j], sp);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -293,16 +303,29 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd) {
 #pragma unroll
       for (int ci = 0; ci < kIPT; ++ci) copy_chunk(cj, ci);
     }
-    // full scores: own partial + the other half's (the same sum in both waves)
-    const float4* other = &part[i & 1][wave ^ 2][0][0];
+    // full scores: the KP partials of this head tile, added as a butterfly
+    // (own + part kh^1, then + (part kh^2 + part kh^3)); every term pair is
+    // commutative, so every wave of the head tile gets the same bits
+    auto other = [&](int q, int r4) -> float4 { return part[i & 1][q * NH + ht][r4][lane]; };
     float s[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const float4 v = other[r4 * 64 + lane];
-      s[4 * r4] = sp[4 * r4] + v.x;
-      s[4 * r4 + 1] = sp[4 * r4 + 1] + v.y;
-      s[4 * r4 + 2] = sp[4 * r4 + 2] + v.z;
-      s[4 * r4 + 3] = sp[4 * r4 + 3] + v.w;
+      float4 v = other(kh ^ 1, r4);
+      if constexpr (KP == 4) {
+        const float4 a = other(kh ^ 2, r4), b2 = other(kh ^ 3, r4);
+        const float4 x = make_float4(sp[4 * r4] + v.x, sp[4 * r4 + 1] + v.y, sp[4 * r4 + 2] + v.z,
+                                     sp[4 * r4 + 3] + v.w);
+        v = make_float4(a.x + b2.x, a.y + b2.y, a.z + b2.z, a.w + b2.w);
+        s[4 * r4] = x.x + v.x;
+        s[4 * r4 + 1] = x.y + v.y;
+        s[4 * r4 + 2] = x.z + v.z;
+        s[4 * r4 + 3] = x.w + v.w;
+      } else {
+        s[4 * r4] = sp[4 * r4] + v.x;
+        s[4 * r4 + 1] = sp[4 * r4 + 1] + v.y;
+        s[4 * r4 + 2] = sp[4 * r4 + 2] + v.z;
+        s[4 * r4 + 3] = sp[4 * r4 + 3] + v.w;
+      }
     }
     // scaled scores (base 2; any finite scale, zero and negative included);
     // register r holds token 8*(r/4) + 4*half + r%4 of the tile
@@ -330,7 +353,7 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd) {
       pn[r >> 3][r & 7] = static_cast<__bf16>(pv);
     }
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < MTW; ++m)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) oacc[m] = mfma(vf[m][jj], pn[jj], oacc[m]);
   };
@@ -350,7 +373,7 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   bool first_pass = true;
   while (true) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < MTW; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[m][r] = 0.f;
     l_part = 0.f;
@@ -387,10 +410,10 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd) {
                                         fp16_partials_scale_offset(p.num_splits, p.batch, p.heads, kDS));
   const float l_tot = both_halves_sum(l_part);
   const int64_t row = row0 + hd;
-  if (kh == 0 && half == 0) p.ws_lse[row] = (m_run + __log2f(l_tot)) * kLn2;
+  if (kh == 0 && half == 0 && real) p.ws_lse[row] = (m_run + __log2f(l_tot)) * kLn2;
   const float inv_l = 1.0f / l_tot;
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {      // 64-column blocks of this wave
+  for (int blk = 0; blk < MTW / 2; ++blk) {   // 64-column blocks of this wave
     float amax = 0.f;
 #pragma unroll
     for (int m = 2 * blk; m < 2 * blk + 2; ++m)
@@ -400,7 +423,7 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     const float hs = amax > 0.f ? 1.0f / amax : 0.f;
 #pragma unroll
     for (int m = 2 * blk; m < 2 * blk + 2; ++m) {
-      uint16_t* dst = wh + row * kDS + 32 * (8 * kh + m) + 4 * half;
+      uint16_t* dst = wh + row * kDS + 32 * (MTW * kh + m) + 4 * half;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint32_t w[2];
@@ -411,17 +434,20 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd) {
           w[k] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
         }
-        *reinterpret_cast<uint2*>(dst + 8 * q) = make_uint2(w[0], w[1]);
+        if (real) *reinterpret_cast<uint2*>(dst + 8 * q) = make_uint2(w[0], w[1]);
       }
     }
-    if (half == 0) wsc[row * (kDS / 64) + 4 * kh + blk] = amax * inv_l;
+    if (half == 0 && real) wsc[row * (kDS / 64) + (MTW / 2) * kh + blk] = amax * inv_l;
   }
 }
 
 }  // namespace
 
+// Groups of 64 heads where the head count allows, else 32, else 16.
+int decode_mla_group_heads(int heads) { return heads % 64 == 0 ? 64 : (heads % 32 == 0 ? 32 : 16); }
+
 bool decode_mla_supported(int heads, int d_s, int d_r, int block_size) {
-  return heads % 64 == 0 && d_s == kDS && d_r == kDR && block_size % kT == 0;
+  return heads % 16 == 0 && d_s == kDS && d_r == kDR && block_size % kT == 0;
 }
 
 int decode_mla_max_chunk() { return kMaxTiles * kT; }
@@ -429,9 +455,13 @@ int decode_mla_max_chunk() { return kMaxTiles * kT; }
 hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t s) {
   if (!decode_mla_supported(p.heads, p.d_s, p.d_r, p.block_size)) return hipErrorNotSupported;
   if (p.chunk > kMaxTiles * kT || p.chunk % kT != 0) return hipErrorInvalidValue;
-  const int n_units = p.num_splits * p.batch * (p.heads / 64);
+  const int hv = decode_mla_group_heads(p.heads);
+  const int n_units = p.num_splits * p.batch * (p.heads / hv);
   const int per_xcd = (n_units + 7) / 8;
-  hipLaunchKernelGGL(decode_mla_kernel, dim3(8 * per_xcd), dim3(kNT), 0, s, p, n_units, per_xcd);
+  if (hv == 64)
+    hipLaunchKernelGGL(decode_mla_kernel<2>, dim3(8 * per_xcd), dim3(kNT), 0, s, p, n_units, per_xcd, hv);
+  else
+    hipLaunchKernelGGL(decode_mla_kernel<1>, dim3(8 * per_xcd), dim3(kNT), 0, s, p, n_units, per_xcd, hv);
   return hipGetLastError();
 }
 

@@ -148,6 +148,7 @@ int decode_latsplit_partial_block();   // columns per scale of its fp16 split ou
 hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t s);
 bool decode_mla_supported(int heads, int d_s, int d_r, int block_size);
 int decode_mla_max_chunk();
+int decode_mla_group_heads(int heads);   // heads per workgroup of the 512-wide kernel
 hipError_t launch_decode_generic(const DecodeParams& p, int is_bf16, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_combine(const PartPtrs& parts, int part_bf16, int tp, int batch, int heads,

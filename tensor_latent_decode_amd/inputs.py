@@ -90,6 +90,13 @@ CONFIGS = {
         desc="plain MLA under TP=2 on one device (the comparison TPLA is measured "
              "against), bf16: B=16, 64 of DeepSeek-V3's 128 heads, the whole "
              "512-wide latent, d_r=64, context 32768, block 64"),
+    "mla_tp4_32k": TplaConfig(
+        "mla_tp4_32k", batch=16, heads=16, d_c=512, tp=1, d_r=64, ctx=32768,
+        scale=1.0 / math.sqrt(192.0), dtype="bf16", block_size=64, seed=7,
+        rms_rows=False,
+        desc="plain MLA under TP=4 on one device (the comparison TPLA is measured "
+             "against), bf16: B=16, 16 of Kimi-K2's 64 heads, the whole 512-wide "
+             "latent, d_r=64, context 32768, block 64"),
     "ragged_tp2": TplaConfig(
         "ragged_tp2", batch=32, heads=128, d_c=512, tp=2, d_r=64,
         ctx=(1024, 32768), scale=1.0 / math.sqrt(192.0), dtype="bf16",

@@ -400,6 +400,8 @@ SHAPES = [  # (heads, d_c, tp, d_r)
     (128, 256, 2, 0),
     (64, 512, 1, 64),       # plain MLA under TP=2: 64 heads, whole latent
     (128, 512, 1, 64),      # plain MLA, one device
+    (48, 512, 1, 64),       # plain MLA in 16-head groups (Kimi-K2 under TP=4 has 16)
+    (96, 512, 1, 64),       # plain MLA in 32-head groups
 ]
 
 
@@ -571,11 +573,12 @@ def mla_reference(case, b: int, n: int):
                              case.cfg.scale)
 
 
+@pytest.mark.parametrize("heads", [64, 16])
 @pytest.mark.parametrize("scale", [-0.07, 0.0, 0.3])
-def test_mla_decode_any_scale(scale):
+def test_mla_decode_any_scale(scale, heads):
     """Zero and negative scales are valid softmax scales (a zero scale is the
     plain mean of the rows)."""
-    case = mla_case(batch=2, ctx=(200, 700), seed=81, scale=scale)
+    case = mla_case(heads=heads, batch=2, ctx=(200, 700), seed=81, scale=scale)
     gc = GpuCase(case)
     o, lse = mla_decode(gc, num_splits=2)
     for b in range(2):
@@ -585,10 +588,12 @@ def test_mla_decode_any_scale(scale):
         assert np.max(np.abs(lse[b] - ref_l)) <= 2e-2
 
 
+@pytest.mark.parametrize("heads", [128, 16, 32])
 @pytest.mark.parametrize("lens", [[1, 31, 32, 33], [63, 64, 65, 95], [96, 97, 2047, 2049]])
-def test_mla_decode_tile_edges(lens):
-    """Lengths at and around the 32-token tile and the 64-token block."""
-    case = mla_case(heads=128, batch=4, ctx=max(lens) + 1, seed=82)
+def test_mla_decode_tile_edges(lens, heads):
+    """Lengths at and around the 32-token tile and the 64-token block, for
+    64-, 16- and 32-head groups."""
+    case = mla_case(heads=heads, batch=4, ctx=max(lens) + 1, seed=82)
     gc = GpuCase(case)
     L = torch.tensor(lens, dtype=torch.int32, device="cuda")
     for splits in (0, 1, 5):
@@ -620,7 +625,7 @@ def test_mla_decode_deterministic_and_strided_query():
 # The workloads at their real sizes (sampled sequences)
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("heads,d_c,tp", [(128, 512, 2), (64, 512, 4), (64, 512, 1)])
+@pytest.mark.parametrize("heads,d_c,tp", [(128, 512, 2), (64, 512, 4), (64, 512, 1), (16, 512, 1)])
 def test_decode_split_longer_than_tile_table(heads, d_c, tp):
     """A single requested split longer than the streaming kernel's tile
     table (65536 tokens) is planned as more splits and stays exact."""
@@ -671,7 +676,7 @@ def test_dsv3_4k_full():
         assert rel_err(host_f64(outs[g])[0], parts[g][0]) <= TOL_BF16
 
 
-@pytest.mark.parametrize("name", ["dsv3_32k", "kimi_k2_32k", "mla_tp2_32k"])
+@pytest.mark.parametrize("name", ["dsv3_32k", "kimi_k2_32k", "mla_tp2_32k", "mla_tp4_32k"])
 def test_32k_shard_sampled(name):
     """One shard (g = 0) at its real shape, automatic splits as the bench runs it."""
     case = make_case(CONFIGS[name])
