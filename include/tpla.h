@@ -233,7 +233,7 @@ typedef struct tpla_decode_args {
   int32_t num_splits;          /* token splits per sequence; 0 = automatic.     */
                                /* A request: raised where a kernel caps the     */
                                /* tokens of one split (65536 on the bf16        */
-                               /* streaming kernel, block_size % 64 == 0)       */
+                               /* streaming kernels)                            */
 } tpla_decode_args;
 
 /*
@@ -285,11 +285,15 @@ tpla_status tpla_decode_suggest_splits(const tpla_decode_args* args, const int32
  *   - the streaming matrix-core kernel serves block_size % 64 == 0, d_r == 64
  *     and either heads % 128 == 0 with d_s == 256 or heads % 64 == 0 with
  *     d_s == 128;
+ *   - a streaming matrix-core kernel for the whole 512-wide latent serves
+ *     d_s == 512, d_r == 64, heads % 16 == 0 and block_size % 32 == 0: plain
+ *     MLA under tensor parallelism (every device keeps the whole latent for
+ *     its heads; TPLA abstract), or one shard at T = 1;
  *   - a register-staged matrix-core kernel serves heads % 32 == 0 with d_s
  *     in {64, 128, 256} and d_r in {0, 64};
  * every other case (and FP32) runs a float32 kernel, which needs
  * 4*(24*(d_s + d_r) + 8*d_s + 152) <= 65536 bytes of LDS (e.g. d_s = 256,
- * d_r = 64 fits; d_s = 512, d_r = 64 does not: TPLA_ERR_UNSUPPORTED).
+ * d_r = 64 fits; d_s = 512, d_r = 64 does not: TPLA_ERR_UNSUPPORTED there).
  * out_dtype FP32 or BF16.
  * workspace: device, at least tpla_decode_workspace_size() bytes, 256-byte
  * aligned; its contents on entry do not matter.
