@@ -42,6 +42,11 @@ is taken:
   the value up-projection: device g holds rows g*d_s .. of every head's
   transposed W_UV (latent index first), rotated like the latent, and its
   up-projected output is summed over devices (reading R11).
+* Prefill keeps the MLA form ([ABS-R]; [BLOG] "Prefill-Decode Separation for
+  Optimal Performance"): no slicing and no rotation; prompt position t of
+  every head attends causally to the prompt's own positions 0..t, with the
+  decode step's score (latent dot product plus rope dot product, times the
+  scale) and the whole latent row as the value (reading R12).
 
 Every function works in float64.  bf16 data enter as their exact values.
 """
@@ -69,6 +74,7 @@ __all__ = [
     "tpla_decode_paged",
     "mla_decode",
     "mla_decode_unabsorbed",
+    "mla_prefill",
     "rms_normalize",
     "slice_rms_normalize",
     "rotate_normalize_latent",
@@ -349,6 +355,37 @@ def mla_decode_unabsorbed(q_nope, q_rope, c_lat, k_rope, w_uk, w_uv, scale: floa
         w = np.exp(s - s.max())
         out[h] = (w / w.sum()) @ vals
     return out
+
+
+# ---------------------------------------------------------------------------
+# MLA-form prefill ([ABS-R]: MLA kept for the compute-bound prefill; [BLOG]
+# "Prefill-Decode Separation for Optimal Performance")
+# ---------------------------------------------------------------------------
+
+def mla_prefill(q_lat, q_rope, c_lat, k_rope, scale: float):
+    """Causal attention of one prompt in the MLA form.
+
+    q_lat [S, H, d_c], q_rope [S, H, d_r], c_lat [S, d_c], k_rope [S, d_r].
+    Position t, head h: s[t, h, j] = scale * (q_lat[t, h] . c_lat[j] +
+    q_rope[t, h] . k_rope[j]) for j <= t (later positions are not seen);
+    softmax over j; the value of position j is its whole latent row.
+    Returns (o [S, H, d_c], lse [S, H]).
+    """
+    q_lat = np.asarray(q_lat, np.float64)
+    q_rope = np.asarray(q_rope, np.float64)
+    c_lat = np.asarray(c_lat, np.float64)
+    k_rope = np.asarray(k_rope, np.float64)
+    S = c_lat.shape[0]
+    s = scale * (np.einsum("thk,jk->thj", q_lat, c_lat) +
+                 np.einsum("thk,jk->thj", q_rope, k_rope))          # [S, H, S]
+    later = np.arange(S)[None, :] > np.arange(S)[:, None]           # [t, j]: j > t
+    s = np.where(later[:, None, :], -np.inf, s)
+    m = s.max(axis=2, keepdims=True)
+    w = np.exp(s - m)
+    l = w.sum(axis=2, keepdims=True)
+    o = np.einsum("thj,jk->thk", w, c_lat) / l
+    lse = (m + np.log(l))[:, :, 0]
+    return o, lse
 
 
 # ---------------------------------------------------------------------------

@@ -547,3 +547,88 @@ def test_rotated_weights_undo_the_latent_rotation():
     # rotate_weight_rows is Hn @ w[h] with the dense library matrix
     Hn = scipy.linalg.hadamard(64) / 8.0
     np.testing.assert_allclose(oracle.rotate_weight_rows(w)[1], Hn @ w[1], rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# MLA-form prefill (causal attention of a prompt over its own latent rows)
+# --------------------------------------------------------------------------
+
+def _prefill_inputs(seed, S=23, H=3, d_c=16, d_r=4):
+    rng = _rng(seed)
+    return (rng.standard_normal((S, H, d_c)), rng.standard_normal((S, H, d_r)),
+            rng.standard_normal((S, d_c)), rng.standard_normal((S, d_r)))
+
+
+def test_prefill_matches_torch_causal_sdpa():
+    # library routine: torch's causal scaled-dot-product attention in float64,
+    # keys = [latent || rope], values = latent, heads as the batch
+    ql, qr, c, r = _prefill_inputs(60)
+    scale = 0.31
+    o, _ = oracle.mla_prefill(ql, qr, c, r, scale)
+    q = torch.from_numpy(np.concatenate([ql, qr], axis=2)).permute(1, 0, 2)      # [H, S, d]
+    k = torch.from_numpy(np.concatenate([c, r], axis=1))[None].expand(q.shape[0], -1, -1)
+    v = torch.from_numpy(c)[None].expand(q.shape[0], -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale)
+    np.testing.assert_allclose(o, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_brute_force_loops():
+    ql, qr, c, r = _prefill_inputs(61, S=6, H=2, d_c=3, d_r=2)
+    scale = 0.7
+    o, lse = oracle.mla_prefill(ql, qr, c, r, scale)
+    for t in range(6):
+        for h in range(2):
+            sc = []
+            for j in range(t + 1):
+                acc = 0.0
+                for k in range(3):
+                    acc += ql[t, h, k] * c[j, k]
+                for k in range(2):
+                    acc += qr[t, h, k] * r[j, k]
+                sc.append(scale * acc)
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            tot = sum(w)
+            assert abs(lse[t, h] - (mx + math.log(tot))) < 1e-12
+            for k in range(3):
+                assert abs(o[t, h, k] - sum(w[j] * c[j, k] for j in range(t + 1)) / tot) < 1e-12
+
+
+def test_prefill_rows_are_decode_steps_over_the_prefix():
+    # position t of the prefill is the decode of t's query over positions 0..t
+    ql, qr, c, r = _prefill_inputs(62)
+    o, lse = oracle.mla_prefill(ql, qr, c, r, 0.2)
+    for t in range(c.shape[0]):
+        ref, ref_l = oracle.mla_decode(ql[t], qr[t], c[:t + 1], r[:t + 1], 0.2)
+        np.testing.assert_allclose(o[t], ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[t], ref_l, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_first_position_and_causality():
+    ql, qr, c, r = _prefill_inputs(63)
+    o, lse = oracle.mla_prefill(ql, qr, c, r, 0.45)
+    # one visible key: its own row exactly, lse = its score
+    for h in range(ql.shape[1]):
+        np.testing.assert_array_equal(o[0, h], c[0])
+        assert abs(lse[0, h] - 0.45 * (ql[0, h] @ c[0] + qr[0, h] @ r[0])) < 1e-12
+    # later rows change nothing at earlier positions
+    c2, r2 = c.copy(), r.copy()
+    c2[10:] += 5.0
+    r2[10:] -= 3.0
+    o2, lse2 = oracle.mla_prefill(ql, qr, c2, r2, 0.45)
+    np.testing.assert_array_equal(o2[:10], o[:10])
+    np.testing.assert_array_equal(lse2[:10], lse[:10])
+    assert np.max(np.abs(o2[10:] - o[10:])) > 1e-3
+
+
+def test_prefill_identical_rows_closed_form():
+    # every row the same: the output is that row and lse = score + log(t + 1)
+    ql, qr, _, _ = _prefill_inputs(64)
+    S = ql.shape[0]
+    row = np.linspace(-1.0, 1.0, 16)
+    rope = np.array([0.5, -0.25, 1.0, 2.0])
+    o, lse = oracle.mla_prefill(ql, qr, np.tile(row, (S, 1)), np.tile(rope, (S, 1)), 0.3)
+    for t in range(S):
+        np.testing.assert_allclose(o[t], np.tile(row, (ql.shape[1], 1)), rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(lse[t], 0.3 * (ql[t] @ row + qr[t] @ rope) + math.log(t + 1),
+                                   rtol=1e-12, atol=1e-12)
