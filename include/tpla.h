@@ -357,6 +357,61 @@ tpla_status tpla_combine_shards(const void* const* partials, tpla_dtype part_dty
                                 int32_t batch, int32_t heads, int32_t d_s, void* out,
                                 tpla_dtype out_dtype, int32_t accumulate, void* stream);
 
+/*
+ * Arguments of an MLA-form prefill (see tpla_mla_prefill).
+ */
+typedef struct tpla_prefill_args {
+  int32_t batch;               /* prompts                                       */
+  int32_t heads;               /* query heads on this device                    */
+  int32_t d_c;                 /* latent width: 512                             */
+  int32_t d_r;                 /* rope width: 64                                */
+  int32_t max_len;             /* positions per prompt in the buffers below     */
+  tpla_dtype dtype;            /* element type of q_latent, q_rope, kv: BF16    */
+  float scale;                 /* softmax scale applied to the whole score      */
+  const void* q_latent;        /* device, absorbed query; element (b,t,h,k) at  */
+  int64_t q_latent_stride_b;   /*   q_latent + b*stride_b + t*stride_t          */
+  int64_t q_latent_stride_t;   /*   + h*stride_h + k                            */
+  int64_t q_latent_stride_h;
+  const void* q_rope;          /* device, rope query, (b,t,h,k) as above        */
+  int64_t q_rope_stride_b;
+  int64_t q_rope_stride_t;
+  int64_t q_rope_stride_h;
+  const void* kv;              /* device, prompt rows [latent (d_c) || rope key */
+  int64_t kv_stride_b;         /*   (d_r)]: row (b,t) at kv + b*stride_b +      */
+  int64_t kv_stride_t;         /*   t*stride_t, d_c + d_r contiguous elements   */
+  const int32_t* seq_lens;     /* device int32 [batch], prompt lengths          */
+  void* out;                   /* device, (b,t,h,k) at out + b*sb + t*st + h*sh */
+  tpla_dtype out_dtype;        /*   + k; FP32 or BF16                           */
+  int64_t out_stride_b;
+  int64_t out_stride_t;
+  int64_t out_stride_h;
+  float* lse;                  /* device float32 [batch, max_len, heads] or NULL */
+} tpla_prefill_args;
+
+/*
+ * tpla_mla_prefill: attention of every prompt position over the prompt, in
+ * the MLA form (no slicing, no rotation).  TPLA keeps MLA for the
+ * compute-bound prefill and switches to the sliced form for decode
+ * (paperbot revised abstract; edgentiq blog, "Prefill-Decode Separation for
+ * Optimal Performance"); the prompt's rows reach the shard caches through
+ * tpla_rotate_append, like decode's new rows.
+ *
+ * For b < batch, t < seq_lens[b] and every head h (causal: positions 0..t):
+ *     s_j = scale * (q_latent[b,t,h,:] . kv[b,j,0:d_c]
+ *                    + q_rope[b,t,h,:] . kv[b,j,d_c:d_c+d_r]),  j <= t
+ *     out[b,t,h,:] = sum_j softmax(s)_j * kv[b,j,0:d_c]
+ *     lse[b,t,h]   = log sum_j exp(s_j)                 (if lse != NULL)
+ * Positions t >= seq_lens[b] (clamped to [0, max_len]) are not written.
+ *
+ * Layout: q_latent, q_rope and kv 16-byte aligned with strides that are
+ * multiples of 8 elements; out 16-byte aligned with strides that are
+ * multiples of 4 elements; kv_stride_t >= d_c + d_r and below 2^26.
+ * Kernel: bf16 matrix cores, 64 (position, head) rows per workgroup.
+ * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE, TPLA_ERR_ALIGN, TPLA_ERR_DTYPE,
+ * TPLA_ERR_UNSUPPORTED (d_c != 512 or d_r != 64), TPLA_ERR_HIP.
+ */
+tpla_status tpla_mla_prefill(const tpla_prefill_args* args, void* stream);
+
 /* Static text for a status code. */
 const char* tpla_status_string(tpla_status status);
 /* Message of the last failed call on this thread ("" if none). */

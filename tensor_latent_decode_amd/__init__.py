@@ -6,4 +6,4 @@ Importing this package does not load the library; the first call does, and
 fails loudly if it is missing.
 """
 
-__version__ = "0.3.0"
+__version__ = "0.4.0"

@@ -256,7 +256,7 @@ const char* tpla_status_string(tpla_status s) {
 
 const char* tpla_last_error(void) { return g_err; }
 
-int32_t tpla_version(void) { return 300; }
+int32_t tpla_version(void) { return 400; }
 
 tpla_status tpla_hadamard_latent(const void* x, tpla_dtype x_dtype, int64_t x_row_stride, void* y,
                                  tpla_dtype y_dtype, int64_t y_row_stride, int64_t rows, int32_t n,
@@ -456,6 +456,61 @@ tpla_status tpla_decode_shard(const tpla_decode_args* a, void* workspace, size_t
   m.out_sh = a->out_stride_h;
   m.lse = a->lse;
   return hip_status(tpla::launch_merge(m, s), "merge launch");
+}
+
+tpla_status tpla_mla_prefill(const tpla_prefill_args* a, void* stream) {
+  if (a == nullptr) return fail(TPLA_ERR_NULL, "args is NULL");
+  if (a->batch < 1 || a->heads < 1 || a->max_len < 0)
+    return fail(TPLA_ERR_SHAPE, "batch and heads must be >= 1 and max_len >= 0");
+  if (a->d_c != 512 || a->d_r != 64)
+    return fail(TPLA_ERR_UNSUPPORTED, "prefill needs d_c = 512 and d_r = 64 (got %d, %d)", a->d_c,
+                a->d_r);
+  if (a->dtype != TPLA_BF16) return fail(TPLA_ERR_DTYPE, "prefill inputs must be TPLA_BF16");
+  if (!valid_dtype(a->out_dtype)) return fail(TPLA_ERR_DTYPE, "out_dtype must be TPLA_FP32 or TPLA_BF16");
+  if (!(a->scale == a->scale) || std::isinf(a->scale)) return fail(TPLA_ERR_SHAPE, "scale must be finite");
+  if (a->q_latent == nullptr || a->q_rope == nullptr || a->kv == nullptr || a->seq_lens == nullptr ||
+      a->out == nullptr)
+    return fail(TPLA_ERR_NULL, "q_latent, q_rope, kv, seq_lens and out are required");
+  const int64_t d = a->d_c + a->d_r;
+  if (a->q_latent_stride_h < a->d_c || a->q_rope_stride_h < a->d_r || a->out_stride_h < a->d_c ||
+      a->kv_stride_t < d || a->kv_stride_t >= (int64_t{1} << 26) || a->q_latent_stride_b < 0 ||
+      a->q_latent_stride_t < 0 || a->q_rope_stride_b < 0 || a->q_rope_stride_t < 0 ||
+      a->kv_stride_b < 0 || a->out_stride_b < 0 || a->out_stride_t < 0)
+    return fail(TPLA_ERR_SHAPE, "strides must cover a row (kv_stride_t in [d_c + d_r, 2^26))");
+  if (static_cast<int64_t>(a->max_len) * a->heads > (int64_t{1} << 36))
+    return fail(TPLA_ERR_SHAPE, "max_len * heads too large");
+  if (!aligned16(a->q_latent) || !aligned16(a->q_rope) || !aligned16(a->kv) || !aligned16(a->out) ||
+      ((a->q_latent_stride_b | a->q_latent_stride_t | a->q_latent_stride_h | a->q_rope_stride_b |
+        a->q_rope_stride_t | a->q_rope_stride_h | a->kv_stride_b | a->kv_stride_t) % 8) != 0 ||
+      ((a->out_stride_b | a->out_stride_t | a->out_stride_h) % 4) != 0)
+    return fail(TPLA_ERR_ALIGN,
+                "q_latent, q_rope, kv and out must be 16-byte aligned; query and kv strides multiples "
+                "of 8 elements, out strides multiples of 4");
+  if (a->max_len == 0) return ok();
+  tpla::PrefillParams p{};
+  p.batch = a->batch;
+  p.heads = a->heads;
+  p.max_len = a->max_len;
+  p.scale_log2 = a->scale * 1.4426950408889634f;
+  p.q_latent = a->q_latent;
+  p.ql_b = a->q_latent_stride_b;
+  p.ql_s = a->q_latent_stride_t;
+  p.ql_h = a->q_latent_stride_h;
+  p.q_rope = a->q_rope;
+  p.qr_b = a->q_rope_stride_b;
+  p.qr_s = a->q_rope_stride_t;
+  p.qr_h = a->q_rope_stride_h;
+  p.kv = a->kv;
+  p.kv_b = a->kv_stride_b;
+  p.kv_s = a->kv_stride_t;
+  p.seq_lens = a->seq_lens;
+  p.out = a->out;
+  p.out_bf16 = a->out_dtype == TPLA_BF16;
+  p.o_b = a->out_stride_b;
+  p.o_s = a->out_stride_t;
+  p.o_h = a->out_stride_h;
+  p.lse = a->lse;
+  return hip_status(tpla::launch_mla_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 
 tpla_status tpla_up_project(const void* o, tpla_dtype o_dtype, int64_t o_stride_b,

@@ -124,7 +124,26 @@ struct UpProjectParams {
   int accumulate;
 };
 
+// MLA-form prefill: causal attention of each prompt over its own latent rows
+// kv[b, j] = [latent (512) || rope key (64)], bf16, 16-byte aligned rows.
+struct PrefillParams {
+  int batch, heads, max_len;
+  float scale_log2;             // scale * log2(e)
+  const void* q_latent;
+  int64_t ql_b, ql_s, ql_h;
+  const void* q_rope;
+  int64_t qr_b, qr_s, qr_h;
+  const void* kv;
+  int64_t kv_b, kv_s;
+  const int32_t* seq_lens;
+  void* out;
+  int out_bf16;
+  int64_t o_b, o_s, o_h;
+  float* lse;                   // [batch, max_len, heads] or null
+};
+
 // Launchers (return the launch status; they do not synchronise).
+hipError_t launch_mla_prefill(const PrefillParams& p, hipStream_t s);
 hipError_t launch_up_project(const UpProjectParams& p, bool o_bf16, bool w_bf16, bool y_bf16,
                              hipStream_t s);
 hipError_t launch_hadamard(const void* x, int x_bf16, int64_t xs, void* y, int y_bf16, int64_t ys,

@@ -32,7 +32,8 @@ from typing import Optional, Tuple, Union
 
 import numpy as np
 
-__all__ = ["TplaConfig", "CONFIGS", "Case", "make_case", "bf16_bits", "BF16_NAN"]
+__all__ = ["TplaConfig", "CONFIGS", "Case", "make_case", "bf16_bits", "BF16_NAN",
+           "PrefillConfig", "PREFILL_CONFIGS", "PrefillCase", "make_prefill_case"]
 
 BF16_NAN = np.uint16(0xFFFF)
 
@@ -233,3 +234,76 @@ def make_case(cfg: TplaConfig, *, batch: Optional[int] = None,
                 q_latent=conv(q_lat), q_rope=conv(q_rope),
                 block_table=block_table, num_blocks=num_blocks,
                 max_blocks=max_blocks)
+
+
+# ---------------------------------------------------------------------------
+# MLA-form prefill inputs: prompts of latent rows [c || k_rope] and their
+# absorbed queries, with the decode cases' value distributions (unit-RMS
+# latent rows, standard normal rope keys and queries).
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    batch: int
+    heads: int
+    d_c: int
+    d_r: int
+    lens: Union[int, Tuple[int, int]]   # prompt length, or (lo, hi) uniform per prompt
+    max_len: int                        # positions in the buffers
+    scale: float
+    seed: int
+    desc: str = ""
+
+
+PREFILL_CONFIGS = {
+    "prefill_small": PrefillConfig(
+        "prefill_small", batch=2, heads=16, d_c=512, d_r=64, lens=(1, 200), max_len=200,
+        scale=1.0 / math.sqrt(192.0), seed=21,
+        desc="small MLA-form prefill: B=2 prompts of 1..200 tokens, 16 heads"),
+    "mla_prefill_4k": PrefillConfig(
+        "mla_prefill_4k", batch=2, heads=64, d_c=512, d_r=64, lens=4096, max_len=4096,
+        scale=1.0 / math.sqrt(192.0), seed=22,
+        desc="MLA-form prefill on one device of DeepSeek-V3 under TP=2: B=2 prompts of 4096 "
+             "tokens, 64 of the 128 heads, latent 512, rope 64"),
+}
+
+
+@dataclass
+class PrefillCase:
+    cfg: PrefillConfig
+    seq_lens: np.ndarray        # [B] int32
+    q_latent: np.ndarray        # [B, S, H, d_c] bf16 bits
+    q_rope: np.ndarray          # [B, S, H, d_r] bf16 bits
+    kv: np.ndarray              # [B, S, d_c + d_r] bf16 bits: [latent || rope key]
+
+
+def make_prefill_case(cfg: PrefillConfig, *, batch: Optional[int] = None,
+                      heads: Optional[int] = None,
+                      lens: Optional[Union[int, Tuple[int, int]]] = None,
+                      max_len: Optional[int] = None, seed: Optional[int] = None) -> PrefillCase:
+    """Draw a batch of prompts for `cfg` (fields may be overridden)."""
+    over = {k: v for k, v in (("batch", batch), ("heads", heads), ("lens", lens),
+                              ("max_len", max_len), ("seed", seed)) if v is not None}
+    if over:
+        cfg = replace(cfg, **over)
+    B, H, d_c, d_r, S = cfg.batch, cfg.heads, cfg.d_c, cfg.d_r, cfg.max_len
+    ss = np.random.SeedSequence(cfg.seed).spawn(5)
+    rngs = [np.random.Generator(np.random.PCG64(x)) for x in ss]
+    if isinstance(cfg.lens, tuple):
+        seq_lens = rngs[0].integers(cfg.lens[0], cfg.lens[1] + 1, size=B).astype(np.int32)
+    else:
+        seq_lens = np.full(B, int(cfg.lens), dtype=np.int32)
+    if np.any(seq_lens > S) or np.any(seq_lens < 0):
+        raise ValueError("prompt lengths must lie in [0, max_len]")
+    kv = np.empty((B, S, d_c + d_r), dtype=np.uint16)
+    q_lat = np.empty((B, S, H, d_c), dtype=np.uint16)
+    q_rope = np.empty((B, S, H, d_r), dtype=np.uint16)
+    for b in range(B):
+        kv[b, :, :d_c] = bf16_bits(_unit_rms(_normal(rngs[1], (S, d_c))))
+        kv[b, :, d_c:] = bf16_bits(_normal(rngs[2], (S, d_r)))
+        for t0 in range(0, S, 256):
+            t1 = min(S, t0 + 256)
+            q_lat[b, t0:t1] = bf16_bits(_normal(rngs[3], (t1 - t0, H, d_c)))
+            q_rope[b, t0:t1] = bf16_bits(_normal(rngs[4], (t1 - t0, H, d_r)))
+    return PrefillCase(cfg=cfg, seq_lens=seq_lens, q_latent=q_lat, q_rope=q_rope, kv=kv)

@@ -51,6 +51,25 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class PrefillArgs(ctypes.Structure):
+    """Mirror of tpla_prefill_args (include/tpla.h)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("d_c", ctypes.c_int32),
+        ("d_r", ctypes.c_int32), ("max_len", ctypes.c_int32), ("dtype", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("q_latent", ctypes.c_void_p), ("q_latent_stride_b", ctypes.c_int64),
+        ("q_latent_stride_t", ctypes.c_int64), ("q_latent_stride_h", ctypes.c_int64),
+        ("q_rope", ctypes.c_void_p), ("q_rope_stride_b", ctypes.c_int64),
+        ("q_rope_stride_t", ctypes.c_int64), ("q_rope_stride_h", ctypes.c_int64),
+        ("kv", ctypes.c_void_p), ("kv_stride_b", ctypes.c_int64), ("kv_stride_t", ctypes.c_int64),
+        ("seq_lens", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int),
+        ("out_stride_b", ctypes.c_int64), ("out_stride_t", ctypes.c_int64),
+        ("out_stride_h", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+    ]
+
+
 class RotateAppendArgs(ctypes.Structure):
     """Mirror of tpla_rotate_append_args (include/tpla.h)."""
     _fields_ = [
@@ -97,9 +116,10 @@ def lib() -> ctypes.CDLL:
     L.tpla_decode_suggest_splits.argtypes = [ctypes.POINTER(DecodeArgs), vp, ctypes.POINTER(i32)]
     L.tpla_up_project.argtypes = [vp, dt, i64, i64, vp, dt, i64, i64, vp, dt, i64, i64,
                                   i32, i32, i32, i32, i32, vp]
+    L.tpla_mla_prefill.argtypes = [ctypes.POINTER(PrefillArgs), vp]
     for f in ("tpla_hadamard_latent", "tpla_append_kv", "tpla_decode_workspace_size",
               "tpla_decode_shard", "tpla_combine_shards", "tpla_rotate_append",
-              "tpla_decode_suggest_splits", "tpla_up_project"):
+              "tpla_decode_suggest_splits", "tpla_up_project", "tpla_mla_prefill"):
         getattr(L, f).restype = ctypes.c_int
     L.tpla_status_string.argtypes = [ctypes.c_int]
     L.tpla_status_string.restype = ctypes.c_char_p
@@ -404,6 +424,55 @@ def decode_shard(q_latent: torch.Tensor, q_rope: Optional[torch.Tensor], cache: 
     nbytes = workspace.numel() * workspace.element_size()
     _check("tpla_decode_shard", lib().tpla_decode_shard(ctypes.byref(args), workspace.data_ptr(),
                                                         nbytes, _stream(q_latent)))
+    return out, lse
+
+
+def make_prefill_args(q_latent: torch.Tensor, q_rope: torch.Tensor, kv: torch.Tensor,
+                      seq_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                      lse: Optional[torch.Tensor] = None) -> PrefillArgs:
+    """Arguments of tpla_mla_prefill from q_latent [B, S, H, d_c], q_rope [B, S, H, d_r],
+    kv [B, S, d_c + d_r] (rows [latent || rope key]), out [B, S, H, d_c]."""
+    B, S, H, d_c = q_latent.shape
+    d_r = q_rope.shape[3]
+    if q_rope.shape[:3] != (B, S, H) or kv.shape[:2] != (B, S) or kv.shape[2] != d_c + d_r:
+        raise ValueError("q_rope must be [B, S, H, d_r] and kv [B, S, d_c + d_r]")
+    if out.shape != (B, S, H, d_c):
+        raise ValueError("out must be [B, S, H, d_c]")
+    for t in (q_latent, q_rope, kv, out):
+        if t.stride(-1) != 1:
+            raise ValueError("last dimension must be contiguous")
+    if lse is not None and (lse.shape != (B, S, H) or not lse.is_contiguous()
+                            or lse.dtype != torch.float32):
+        raise ValueError("lse must be contiguous float32 [B, S, H]")
+    a = PrefillArgs()
+    a.batch, a.heads, a.d_c, a.d_r, a.max_len = B, H, d_c, d_r, S
+    a.dtype, a.scale = _dt(q_latent), float(scale)
+    a.q_latent = q_latent.data_ptr()
+    a.q_latent_stride_b, a.q_latent_stride_t, a.q_latent_stride_h = q_latent.stride()[:3]
+    a.q_rope = q_rope.data_ptr()
+    a.q_rope_stride_b, a.q_rope_stride_t, a.q_rope_stride_h = q_rope.stride()[:3]
+    a.kv = kv.data_ptr()
+    a.kv_stride_b, a.kv_stride_t = kv.stride()[:2]
+    a.seq_lens = seq_lens.data_ptr()
+    a.out, a.out_dtype = out.data_ptr(), _dt(out)
+    a.out_stride_b, a.out_stride_t, a.out_stride_h = out.stride()[:3]
+    a.lse = lse.data_ptr() if lse is not None else None
+    return a
+
+
+def mla_prefill(q_latent: torch.Tensor, q_rope: torch.Tensor, kv: torch.Tensor,
+                seq_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32):
+    """MLA-form prefill of a batch of prompts.  Returns (out [B, S, H, d_c], lse or None);
+    positions at or past seq_lens[b] are left as they were in `out`."""
+    _gpu(q_latent, q_rope, kv, seq_lens, out, lse)
+    B, S, H, d_c = q_latent.shape
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+        raise ValueError("seq_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, S, H, d_c), dtype=out_dtype, device=q_latent.device)
+    args = make_prefill_args(q_latent, q_rope, kv, seq_lens, scale, out, lse)
+    _check("tpla_mla_prefill", lib().tpla_mla_prefill(ctypes.byref(args), _stream(q_latent)))
     return out, lse
 
 

@@ -19,7 +19,7 @@ def test_exports_every_declared_function():
     assert {"tpla_hadamard_latent", "tpla_append_kv", "tpla_decode_workspace_size",
             "tpla_decode_shard", "tpla_combine_shards", "tpla_status_string",
             "tpla_last_error", "tpla_version", "tpla_rotate_append",
-            "tpla_decode_suggest_splits", "tpla_up_project"} <= set(names)
+            "tpla_decode_suggest_splits", "tpla_up_project", "tpla_mla_prefill"} <= set(names)
     raw = ctypes.CDLL(tpla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -27,7 +27,7 @@ def test_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = tpla.lib()
-    assert tpla.version() == 300
+    assert tpla.version() == 400
     for code in range(8):
         assert L.tpla_status_string(code)
     assert L.tpla_status_string(99) == b"unknown status"
@@ -232,3 +232,43 @@ def test_up_project_argument_checks():
     _fails(call(o=None), 1)
     _fails(call(w=None), 1)
     _fails(call(y=None), 1)
+
+
+def _prefill_args():
+    a = tpla.PrefillArgs()
+    a.batch, a.heads, a.d_c, a.d_r, a.max_len = 2, 64, 512, 64, 100
+    a.dtype, a.scale = 1, 0.07
+    a.q_latent, a.q_latent_stride_b, a.q_latent_stride_t, a.q_latent_stride_h = FAKE, 100 * 64 * 512, 64 * 512, 512
+    a.q_rope, a.q_rope_stride_b, a.q_rope_stride_t, a.q_rope_stride_h = FAKE, 100 * 64 * 64, 64 * 64, 64
+    a.kv, a.kv_stride_b, a.kv_stride_t = FAKE, 100 * 576, 576
+    a.seq_lens = FAKE
+    a.out, a.out_dtype = FAKE, 0
+    a.out_stride_b, a.out_stride_t, a.out_stride_h = 100 * 64 * 512, 64 * 512, 512
+    a.lse = None
+    return a
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, 2), ("heads", 0, 2), ("max_len", -1, 2),
+    ("d_c", 256, 5), ("d_r", 0, 5),
+    ("dtype", 0, 4), ("out_dtype", 9, 4),
+    ("scale", float("nan"), 2), ("scale", float("inf"), 2),
+    ("q_latent", None, 1), ("q_rope", None, 1), ("kv", None, 1), ("seq_lens", None, 1),
+    ("out", None, 1),
+    ("q_latent_stride_h", 256, 2), ("q_rope_stride_h", 32, 2), ("kv_stride_t", 512, 2),
+    ("kv_stride_t", 1 << 26, 2), ("out_stride_h", 500, 2), ("kv_stride_b", -8, 2),
+    ("q_latent", FAKE + 8, 3), ("kv", FAKE + 4, 3), ("out", FAKE + 8, 3),
+    ("q_latent_stride_t", 64 * 512 + 4, 3), ("kv_stride_t", 580, 3), ("out_stride_h", 514, 3),
+])
+def test_prefill_argument_checks(field, value, code):
+    a = _prefill_args()
+    setattr(a, field, value)
+    _fails(tpla.lib().tpla_mla_prefill(ctypes.byref(a), None), code)
+
+
+def test_prefill_null_args_and_empty():
+    L = tpla.lib()
+    _fails(L.tpla_mla_prefill(None, None), 1)
+    a = _prefill_args()
+    a.max_len = 0
+    assert L.tpla_mla_prefill(ctypes.byref(a), None) == 0     # nothing to do, nothing touched

@@ -789,3 +789,147 @@ def test_up_project_aligned_float32_partial_kstep(d_s):
     torch.cuda.synchronize()
     ref = oracle.up_project_shard(host_f64(o), host_f64(w).transpose(0, 2, 1))
     assert rel_err(host_f64(y), ref) <= TOL_FP32
+
+
+# --------------------------------------------------------------------------
+# MLA-form prefill (tpla_mla_prefill)
+# --------------------------------------------------------------------------
+
+from tensor_latent_decode_amd.inputs import PREFILL_CONFIGS, make_prefill_case  # noqa: E402
+
+SENTINEL = 7.0
+
+
+def prefill_ref(pc, b):
+    """The oracle's causal MLA attention over prompt b."""
+    L = int(pc.seq_lens[b])
+    kv = as_f64(pc.kv[b, :L])
+    d_c = pc.cfg.d_c
+    return oracle.mla_prefill(as_f64(pc.q_latent[b, :L]), as_f64(pc.q_rope[b, :L]), kv[:, :d_c],
+                              kv[:, d_c:], pc.cfg.scale)
+
+
+def run_prefill(pc, out_dtype=torch.float32, lens=None):
+    B, S, H, d_c = pc.q_latent.shape
+    out = torch.full((B, S, H, d_c), SENTINEL, dtype=out_dtype, device="cuda")
+    lse = torch.full((B, S, H), SENTINEL, dtype=torch.float32, device="cuda")
+    lens = dev(pc.seq_lens) if lens is None else lens
+    tpla.mla_prefill(dev(pc.q_latent), dev(pc.q_rope), dev(pc.kv), lens, pc.cfg.scale, out=out,
+                     lse=lse)
+    torch.cuda.synchronize()
+    return host_f64(out), host_f64(lse)
+
+
+@pytest.mark.parametrize("heads", [16, 64, 128, 3, 40])
+@pytest.mark.parametrize("out_dt", [torch.float32, torch.bfloat16])
+def test_prefill_parity(heads, out_dt):
+    """Every position of ragged prompts against the oracle; heads that are not
+    a multiple of 64 put several positions into one workgroup's rows."""
+    pc = make_prefill_case(PREFILL_CONFIGS["prefill_small"], heads=heads, seed=90 + heads)
+    out, lse = run_prefill(pc, out_dt)
+    for b in range(pc.cfg.batch):
+        L = int(pc.seq_lens[b])
+        ref_o, ref_l = prefill_ref(pc, b)
+        assert rel_err(out[b, :L], ref_o) <= TOL_BF16, (b, L)
+        assert np.max(np.abs(lse[b, :L] - ref_l)) <= 2e-2, (b, L)
+        assert np.all(out[b, L:] == SENTINEL) and np.all(lse[b, L:] == SENTINEL)
+
+
+def test_prefill_tile_edge_lengths_and_empty_prompt():
+    pc = make_prefill_case(PREFILL_CONFIGS["prefill_small"], batch=6, heads=64, lens=97,
+                           max_len=97, seed=95)
+    lens_host = np.array([0, 1, 31, 32, 33, 97], dtype=np.int32)
+    pc.seq_lens = lens_host
+    out, lse = run_prefill(pc)
+    assert np.all(out[0] == SENTINEL) and np.all(lse[0] == SENTINEL)
+    for b in range(1, 6):
+        L = int(lens_host[b])
+        ref_o, ref_l = prefill_ref(pc, b)
+        assert rel_err(out[b, :L], ref_o) <= TOL_BF16, L
+        assert np.max(np.abs(lse[b, :L] - ref_l)) <= 2e-2, L
+        assert np.all(out[b, L:] == SENTINEL)
+
+
+def test_prefill_late_score_spike():
+    """A key far inside the prompt scores ~260 (base-2 units) above everything
+    before it for one row: a softmax that kept the first tile's max would
+    overflow; every row must still match the oracle."""
+    pc = make_prefill_case(PREFILL_CONFIGS["prefill_small"], batch=1, heads=64, lens=180,
+                           max_len=180, seed=96)
+    q0 = as_f64(pc.q_latent[0, 170, 5])
+    k = 2500.0 / (pc.cfg.scale * float(q0 @ q0))
+    from tensor_latent_decode_amd.inputs import bf16_bits
+    pc.kv[0, 130, :512] = bf16_bits((k * q0).astype(np.float32))
+    out, lse = run_prefill(pc)
+    ref_o, ref_l = prefill_ref(pc, 0)
+    for t in (129, 130, 170, 179):
+        for h in (0, 5, 63):
+            assert rel_err(out[0, t, h], ref_o[t, h]) <= TOL_BF16, (t, h)
+    assert rel_err(out[0], ref_o) <= TOL_BF16
+    assert np.max(np.abs(lse[0] - ref_l)) <= 2e-2
+
+
+def test_prefill_strided_buffers_give_the_same_bits():
+    pc = make_prefill_case(PREFILL_CONFIGS["prefill_small"], heads=16, seed=97)
+    B, S, H, d_c = pc.q_latent.shape
+    base, _ = run_prefill(pc)
+    wq = torch.zeros((B, S, H, 640), dtype=torch.bfloat16, device="cuda")
+    wq[..., 64:576] = dev(pc.q_latent)
+    wr = torch.zeros((B, S, H, 72), dtype=torch.bfloat16, device="cuda")
+    wr[..., 8:72] = dev(pc.q_rope)
+    wkv = torch.zeros((B, S, 640), dtype=torch.bfloat16, device="cuda")
+    wkv[..., :576] = dev(pc.kv)
+    wout = torch.full((B, S, H, 520), SENTINEL, dtype=torch.float32, device="cuda")
+    tpla.mla_prefill(wq[..., 64:576], wr[..., 8:72], wkv[..., :576], dev(pc.seq_lens), pc.cfg.scale,
+                     out=wout[..., :512])
+    torch.cuda.synchronize()
+    got = host_f64(wout)
+    assert np.array_equal(got[..., :512], base)
+    assert np.all(got[..., 512:] == SENTINEL)
+
+
+def test_prefill_4k_sampled():
+    """The benchmarked shape (64 heads, 4096-token prompts), one prompt;
+    sampled positions against the oracle's decode over the prefix (the
+    prefill row identity pinned in the oracle tests)."""
+    pc = make_prefill_case(PREFILL_CONFIGS["mla_prefill_4k"], batch=1)
+    out, lse = run_prefill(pc)
+    kv = as_f64(pc.kv[0])
+    for t in (0, 1, 31, 32, 33, 1000, 2047, 4095):
+        ref_o, ref_l = oracle.mla_decode(as_f64(pc.q_latent[0, t]), as_f64(pc.q_rope[0, t]),
+                                         kv[:t + 1, :512], kv[:t + 1, 512:], pc.cfg.scale)
+        assert rel_err(out[0, t], ref_o) <= TOL_BF16, t
+        assert np.max(np.abs(lse[0, t] - ref_l)) <= 2e-2, t
+
+
+def test_prefill_then_tpla_decode():
+    """The hand-off: the prompt's rows go into the two shard caches through
+    tpla_rotate_append, the next token's row is appended, and the TPLA decode
+    of the next query over the whole prompt matches the oracle's TPLA decode."""
+    pc = make_prefill_case(PREFILL_CONFIGS["prefill_small"], batch=2, heads=64, lens=150,
+                           max_len=151, seed=98)
+    B, S, H, d_c = pc.q_latent.shape
+    tp, d_s, bs = 2, 256, 64
+    L = 150                                     # prompt; position 150 is the next token
+    _, _ = run_prefill(pc)
+    nb = (S + bs - 1) // bs
+    bt = torch.arange(B * nb, dtype=torch.int32, device="cuda").view(B, nb)
+    caches = [torch.zeros((B * nb, bs, d_s + 64), dtype=torch.bfloat16, device="cuda")
+              for _ in range(tp)]
+    kv = dev(pc.kv)
+    rows = kv[:, :L + 1].reshape(B * (L + 1), 576)
+    seq = torch.arange(B, dtype=torch.int32, device="cuda").repeat_interleave(L + 1)
+    pos = torch.arange(L + 1, dtype=torch.int32, device="cuda").repeat(B)
+    tpla.rotate_append(None, None, rows[:, :512], rows[:, 512:], seq, pos, caches, bt)
+    q_next = dev(np.ascontiguousarray(pc.q_latent[:, L]))
+    qr_next = dev(np.ascontiguousarray(pc.q_rope[:, L]))
+    q_rot = tpla.hadamard_latent(q_next)
+    lens = torch.full((B,), L + 1, dtype=torch.int32, device="cuda")
+    outs = [tpla.decode_shard(q_rot[:, :, g * d_s:(g + 1) * d_s], qr_next, caches[g], bt, lens,
+                              pc.cfg.scale, L + 1)[0] for g in range(tp)]
+    got = host_f64(tpla.combine_shards(outs))
+    for b in range(B):
+        kvb = as_f64(pc.kv[b, :L + 1])
+        ref = oracle.tpla_decode(as_f64(pc.q_latent[b, L]), as_f64(pc.q_rope[b, L]), kvb[:, :512],
+                                 kvb[:, 512:], tp, pc.cfg.scale, hadamard=True)
+        assert rel_err(got[b], ref) <= TOL_BF16, b
