@@ -36,6 +36,13 @@ Prints one JSON line.  `value` is the latent-cache bytes the step streams
 back-to-back launches on its own stream right after the timed steps;
 `cpu_baseline` times the fp64 oracle on the host over a bounded sample.
 
+`--mode prefill` (or `--workload mla_prefill_4k`) measures the MLA-form
+prefill instead: tpla_mla_prefill over B=2 prompts of 4096 tokens with 64
+heads, plus the hand-off of the prompt rows into two TPLA shard caches
+(tpla_rotate_append); `value` is the attention's algorithmic TFLOP/s over
+the whole step and `roofline` the attention kernel against the dense bf16
+matrix-core peak.
+
 `--mode copy` runs a plain 1 GiB device copy (for calibrating rocprofv3
 FETCH_SIZE/WRITE_SIZE counters); `--mode decode` runs only decode launches.
 """
@@ -66,8 +73,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv3_32k",
                     choices=["dsv3_32k", "kimi_k2_32k", "ragged_tp2", "dsv3_4k", "mla_tp2_32k",
-                             "mla_tp4_32k"])
-    ap.add_argument("--mode", default="step", choices=["step", "decode", "copy"])
+                             "mla_tp4_32k", "mla_prefill_4k"])
+    ap.add_argument("--mode", default="step", choices=["step", "decode", "copy", "prefill"])
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = auto)")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--up-project", type=int, default=0, metavar="D_V",
@@ -183,6 +190,139 @@ def cpu_baseline(case, seconds: float):
                       f"{done_seqs / elapsed:.3g}"}
 
 
+PREFILL_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix cores, vendor figure
+
+
+def prefill_flops(lens, heads: int, d_c: int, d_r: int) -> int:
+    """Algorithmic FLOPs of causal MLA attention: position t of every head
+    scores t+1 keys over d_c + d_r and sums t+1 values over d_c."""
+    return sum(heads * (int(L) * (int(L) + 1) // 2) * 2 * (2 * d_c + d_r) for L in lens)
+
+
+def cpu_prefill_baseline(pc, seconds: float):
+    """The fp64 oracle on a bounded sample: prefixes of the first prompt,
+    doubled in length until the time budget is spent."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:           # pragma: no cover - threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    f64 = oracle.bf16_bits_to_f64
+    d_c = pc.cfg.d_c
+    n, done, elapsed, dt = 64, 0, 0.0, 0.0
+    # the next prefix costs about 4x the last one: stop before it would
+    # overrun the budget by half
+    while elapsed + 4 * dt < 1.5 * seconds and n <= int(pc.seq_lens[0]):
+        kv = f64(pc.kv[0, :n])
+        ql, qr = f64(pc.q_latent[0, :n]), f64(pc.q_rope[0, :n])
+        t0 = time.perf_counter()
+        oracle.mla_prefill(ql, qr, kv[:, :d_c], kv[:, d_c:], pc.cfg.scale)
+        dt = time.perf_counter() - t0
+        elapsed += dt
+        done += prefill_flops([n], pc.cfg.heads, d_c, pc.cfg.d_r)
+        last = n
+        n *= 2
+    return {"value": done / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"prefixes of 64..{last} tokens of the first prompt (all {pc.cfg.heads} heads), "
+                      f"{elapsed:.1f} s on the host"}
+
+
+def run_prefill(args, torch):
+    import numpy as np
+    from tensor_latent_decode_amd import tpla
+    from tensor_latent_decode_amd.inputs import PREFILL_CONFIGS, make_prefill_case
+
+    t_setup = time.perf_counter()
+    pc = make_prefill_case(PREFILL_CONFIGS["mla_prefill_4k"])
+    cfg = pc.cfg
+    B, S, H, d_c, d_r = cfg.batch, cfg.max_len, cfg.heads, cfg.d_c, cfg.d_r
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    q, qr, kv = dev(pc.q_latent), dev(pc.q_rope), dev(pc.kv)
+    lens = torch.from_numpy(pc.seq_lens).cuda()
+    out = torch.empty((B, S, H, d_c), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, S, H), dtype=torch.float32, device="cuda")
+    # the hand-off: prompt rows rotated, sliced and appended to two shard caches
+    tp, d_s, bs = 2, d_c // 2, 64
+    nb = (S + bs - 1) // bs
+    bt = torch.arange(B * nb, dtype=torch.int32, device="cuda").view(B, nb)
+    caches = [torch.empty((B * nb, bs, d_s + d_r), dtype=torch.bfloat16, device="cuda")
+              for _ in range(tp)]
+    rows = kv.reshape(B * S, d_c + d_r)
+    seq = torch.arange(B, dtype=torch.int32, device="cuda").repeat_interleave(S)
+    pos = torch.arange(S, dtype=torch.int32, device="cuda").repeat(B)
+    stream = torch.cuda.Stream()
+
+    def attention():
+        tpla.mla_prefill(q, qr, kv, lens, cfg.scale, out=out, lse=lse)
+
+    def step():
+        attention()
+        tpla.rotate_append(None, None, rows[:, :d_c], rows[:, d_c:], seq, pos, caches, bt)
+
+    with torch.cuda.stream(stream):
+        step()
+        torch.cuda.synchronize()
+        setup_s = time.perf_counter() - t_setup
+        t_w = time.perf_counter()
+        n_w = 0
+        while n_w < max(args.warmup, 2) or time.perf_counter() - t_w < WARM_SECONDS:
+            step()
+            n_w += 1
+            if n_w % 4 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        steps = max(1, args.steps // 10)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_step = e0.elapsed_time(e1) / steps
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(steps):
+            attention()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        ms_att = a0.elapsed_time(a1) / steps
+    flops = prefill_flops(pc.seq_lens, H, d_c, d_r)
+    result = {
+        "metric": "MLA-form prefill: attention TFLOP/s (bf16 matrix cores) at 4K prompts",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "warmup_steps_run": n_w,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "heads": H, "d_c": d_c, "d_r": d_r,
+                   "prompt_len": S, "global_batch": B, "seq_len": S, "out_dtype": "bf16",
+                   "handoff_shards": tp},
+        "prompt_tokens_per_s": round(B * S / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(flops / (ms_att * 1e-3) / 1e12, 1),
+                     "peak": PREFILL_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (ms_att * 1e-3) / 1e12 / PREFILL_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "tpla_mla_prefill",
+                     "ms_per_launch": round(ms_att, 4), "algorithmic_flops_per_launch": flops},
+        "setup_s": round(setup_s, 1),
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_prefill_baseline(pc, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -204,6 +344,9 @@ def main():
     torch.cuda.set_device(0)
     if args.mode == "copy":
         run_copy(torch, max(args.steps, 1))
+        return
+    if args.mode == "prefill" or args.workload == "mla_prefill_4k":
+        run_prefill(args, torch)
         return
 
     t_setup = time.perf_counter()
