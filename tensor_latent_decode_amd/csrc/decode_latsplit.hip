@@ -213,6 +213,14 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   // issued together instead of after the length check.
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) asm volatile("" : : "v"(qf[kk]));
+  if (p.scale_log2 < 0.f) {     // scores of -q with |scale| are the scores of q with scale
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      uint4 w = __builtin_bit_cast(uint4, qf[kk]);
+      w.x ^= 0x80008000u; w.y ^= 0x80008000u; w.z ^= 0x80008000u; w.w ^= 0x80008000u;
+      qf[kk] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
 #pragma unroll
   for (int k = 0; k < kFill; ++k) asm volatile("" : : "v"(fpg[k]));
   asm volatile("" : : "s"(pg[0]), "s"(pg[1]), "s"(L));
@@ -329,7 +337,11 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   float m_run = -INFINITY;   // reference max of the scaled (base-2) scores
   float l_part = 0.f;        // this lane's share of its head's row sum
   float m_seen;              // largest tile max that overflowed
-  const float c = p.scale_log2;
+  // The softmax below takes a tile's max before scaling, which needs a
+  // positive scale: a negative one is carried by the query instead (its
+  // fragments were negated at load, exactly), and a zero one becomes 2^-100,
+  // which leaves every score's weight exactly 1 (masked ones stay -inf).
+  const float c = p.scale_log2 == 0.f ? 0x1p-100f : fabsf(p.scale_log2);
 
   // Scores of the tile at T and the V^T fragments of this wave's latent
   // tiles; k-steps in rotated order with the A reads two k-steps ahead.

@@ -456,6 +456,27 @@ def test_decode_bf16_late_score_spike(shape, bs):
             assert rel_err(got[b, h], ref[h]) <= TOL_BF16, (b, h)
 
 
+@pytest.mark.parametrize("shape", [(128, 512, 2, 64), (64, 512, 4, 64), (32, 128, 2, 64), (5, 80, 2, 8)])
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+def test_decode_zero_and_negative_scale(shape, scale):
+    """Every decode kernel (the two streaming shapes, the register-staged one,
+    the float32 one) takes any finite scale: a zero scale averages the rows,
+    a negative one favours the lowest scores."""
+    H, d_c, tp, d_r = shape
+    from dataclasses import replace
+    cfg = replace(CONFIGS["dsv3_4k"], heads=H, d_c=d_c, tp=tp, d_r=d_r, scale=scale)
+    case = make_case(cfg, batch=3, ctx=(1, 400), seed=88 + H)
+    gc = GpuCase(case)
+    rot = (d_c & (d_c - 1)) == 0              # the rotation needs a power-of-two width
+    combined, outs, lses = run_step(gc, hadamard=rot, num_splits=2)
+    got = host_f64(combined)
+    for b in range(cfg.batch):
+        ref, parts = oracle_step(case, b, tp, hadamard=rot)
+        assert rel_err(got[b], ref) <= TOL_BF16, (b, int(case.seq_lens[b]))
+        for g, (o, l) in enumerate(parts):
+            assert np.max(np.abs(host_f64(lses[g])[b] - l)) <= 2e-2
+
+
 def test_suggested_splits_uniform_and_ragged():
     """The host-side split suggestion keeps the automatic count for uniform
     32K lengths (DeepSeek-V3 and Kimi-K2 shards), and a ragged batch decoded
