@@ -329,7 +329,7 @@ def main():
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
               f"{world}): TPLA shards would sit on separate GPUs joined by an RCCL "
-              "collective, which this build does not run.", file=sys.stderr)
+              "collective, which this benchmark does not run.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

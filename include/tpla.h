@@ -51,7 +51,7 @@ typedef enum tpla_status {
   TPLA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent          */
   TPLA_ERR_ALIGN = 3,       /* pointer/stride alignment the kernel needs       */
   TPLA_ERR_DTYPE = 4,       /* unsupported element type or combination         */
-  TPLA_ERR_UNSUPPORTED = 5, /* valid request this build has no kernel for      */
+  TPLA_ERR_UNSUPPORTED = 5, /* valid request no kernel of the library serves   */
   TPLA_ERR_WORKSPACE = 6,   /* workspace missing or too small                  */
   TPLA_ERR_HIP = 7          /* the HIP runtime reported an error               */
 } tpla_status;
