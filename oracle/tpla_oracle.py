@@ -260,7 +260,8 @@ def shard_slice(x: np.ndarray, g: int, tp: int) -> np.ndarray:
     return x[..., g * d_s:(g + 1) * d_s]
 
 
-def tpla_shards(q_lat, q_rope, c_lat, k_rope, tp: int, scale: float, hadamard: bool):
+def tpla_shards(q_lat, q_rope, c_lat, k_rope, tp: int, scale: float, hadamard: bool,
+                rope_split: bool = False, latent_mult: float = 1.0):
     """Per-shard outputs of TPLA for one sequence.
 
     q_lat [H, d_c] (absorbed query, latent space), q_rope [H, d_r],
@@ -269,13 +270,23 @@ def tpla_shards(q_lat, q_rope, c_lat, k_rope, tp: int, scale: float, hadamard: b
     over the full latent width.  Step 2: slice both along the latent into tp
     shards; every head keeps all its shards.  Step 3: each shard attends on
     its own (own softmax).  Returns a list of (o_g [H, d_s], lse_g [H]).
+
+    Two other readings of the pages, for diagnostics only (the defaults are
+    readings R1 and R2): rope_split gives each shard its d_r / tp slice of
+    the rope query and key instead of the whole rope; latent_mult multiplies
+    each shard's latent score term (latent_mult = tp makes a shard's partial
+    score an estimate of the whole latent score).
     """
     if hadamard:
         q_lat = fwht(q_lat)
         c_lat = fwht(c_lat)
-    return [shard_attention(shard_slice(q_lat, g, tp), q_rope,
-                            shard_slice(c_lat, g, tp), k_rope, scale)
-            for g in range(tp)]
+    out = []
+    for g in range(tp):
+        qr, kr = ((shard_slice(q_rope, g, tp), shard_slice(k_rope, g, tp)) if rope_split
+                  else (q_rope, k_rope))
+        out.append(shard_attention(latent_mult * shard_slice(q_lat, g, tp), qr,
+                                   shard_slice(c_lat, g, tp), kr, scale))
+    return out
 
 
 def combine_shards(o_shards) -> np.ndarray:

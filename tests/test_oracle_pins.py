@@ -632,3 +632,74 @@ def test_prefill_identical_rows_closed_form():
         np.testing.assert_allclose(o[t], np.tile(row, (ql.shape[1], 1)), rtol=1e-13, atol=1e-13)
         np.testing.assert_allclose(lse[t], 0.3 * (ql[t] @ row + qr[t] @ rope) + math.log(t + 1),
                                    rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Other readings of the pages (diagnostic flags) and the TPLA-vs-MLA gap
+# --------------------------------------------------------------------------
+
+def test_alternative_readings_reduce_to_the_default():
+    rng = _rng(70)
+    ql, qr = rng.standard_normal((3, 32)), rng.standard_normal((3, 8))
+    c, r = rng.standard_normal((40, 32)), rng.standard_normal((40, 8))
+    base = oracle.tpla_shards(ql, qr, c, r, 2, 0.3, True)
+    same = oracle.tpla_shards(ql, qr, c, r, 2, 0.3, True, rope_split=False, latent_mult=1.0)
+    for (o1, l1), (o2, l2) in zip(base, same):
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
+    # one shard: the rope "slice" is the whole rope
+    one = oracle.tpla_shards(ql, qr, c, r, 1, 0.3, False, rope_split=True)
+    ref, _ = oracle.mla_decode(ql, qr, c, r, 0.3)
+    np.testing.assert_allclose(one[0][0], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_alternative_readings_brute_force():
+    # shard g's score with both flags: scale * (m * q_g . c_g + qr_g . r_g),
+    # written out with loops on a tiny case
+    rng = _rng(71)
+    H, L, d_c, d_r, tp, m, sc = 2, 5, 8, 4, 2, 2.0, 0.4
+    ql, qr = rng.standard_normal((H, d_c)), rng.standard_normal((H, d_r))
+    c, r = rng.standard_normal((L, d_c)), rng.standard_normal((L, d_r))
+    parts = oracle.tpla_shards(ql, qr, c, r, tp, sc, False, rope_split=True, latent_mult=m)
+    d_s, d_rs = d_c // tp, d_r // tp
+    for g in range(tp):
+        for h in range(H):
+            s = [sc * (m * sum(ql[h, g * d_s + k] * c[j, g * d_s + k] for k in range(d_s)) +
+                       sum(qr[h, g * d_rs + k] * r[j, g * d_rs + k] for k in range(d_rs)))
+                 for j in range(L)]
+            mx = max(s)
+            w = [math.exp(x - mx) for x in s]
+            for k in range(d_s):
+                want = sum(w[j] * c[j, g * d_s + k] for j in range(L)) / sum(w)
+                assert abs(parts[g][0][h, k] - want) < 1e-12
+
+
+def _cos_to_mla(q, qr, c, r, tp, scale, hadamard, **kw):
+    ref, _ = oracle.mla_decode(q, qr, c, r, scale)
+    parts = oracle.tpla_shards(q, qr, c, r, tp, scale, hadamard, **kw)
+    out = oracle.combine_shards([o for o, _ in parts])
+    if hadamard:
+        out = oracle.fwht(out)
+    return float(np.mean([ref[h] @ out[h] / np.linalg.norm(ref[h]) / np.linalg.norm(out[h])
+                          for h in range(q.shape[0])]))
+
+
+def test_tpla_vs_mla_gap_diagnostic():
+    """Parity unpinned: TPLA with T > 1 approximates MLA and the pages give no
+    closed form for the gap.  What the mathematics fixes: T = 1 is MLA
+    exactly; on iid Gaussian data the rotation changes nothing in
+    distribution.  The values (cosine of TPLA's head outputs to MLA's,
+    H = 16, L = 2048, d_c = 512, d_r = 64) are printed for the record."""
+    rng = _rng(72)
+    H, L, d_c, d_r, scale = 16, 2048, 512, 64, 1 / math.sqrt(192.0)
+    q, qr = rng.standard_normal((H, d_c)), rng.standard_normal((H, d_r))
+    c, r = rng.standard_normal((L, d_c)), rng.standard_normal((L, d_r))
+    assert abs(_cos_to_mla(q, qr, c, r, 1, scale, True) - 1.0) < 1e-12
+    iid = {h: _cos_to_mla(q, qr, c, r, 2, scale, h) for h in (False, True)}
+    assert abs(iid[False] - iid[True]) < 0.02, iid
+    q2, c2 = q.copy(), c.copy()
+    q2[:, :8] *= 10.0                 # 8 outlier channels in query and latent
+    c2[:, :8] *= 10.0
+    out = {h: _cos_to_mla(q2, qr, c2, r, 2, scale, h) for h in (False, True)}
+    print(f"cosine to MLA, T=2: iid {iid}, outlier channels {out}")
+    assert all(0.5 < v < 1.0 for v in list(iid.values()) + list(out.values()))
