@@ -15,7 +15,10 @@
  * memory bound, so the latent cache each device streams is the cost.
  *
  * One call of tpla_decode_shard is one device's share of one decode step:
- * every head, every sequence, one latent slice.
+ * every head, every sequence, one latent slice (with the whole 512-wide
+ * latent it is plain MLA under tensor parallelism, the scheme TPLA is
+ * compared against).  tpla_mla_prefill is the other phase: TPLA keeps the
+ * MLA form for the compute-bound prefill and slices only for decode.
  *
  * Conventions for every entry point:
  *  - The caller owns all memory.  Pointers marked "device" point to GPU
