@@ -397,8 +397,7 @@ def main():
     # split count from the host's copy of the lengths (a serving loop has them)
     splits = args.num_splits or tpla.decode_suggest_splits(args0, case.seq_lens)
     args0.num_splits = splits
-    ws_bytes = tpla.decode_workspace_size(args0)
-    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    workspace = tpla.decode_workspace(args0)
     torch.cuda.synchronize()
 
     def decode(r, i, g):

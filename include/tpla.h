@@ -299,12 +299,15 @@ tpla_status tpla_decode_suggest_splits(const tpla_decode_args* args, const int32
  * d_r = 64 fits; d_s = 512, d_r = 64 does not: TPLA_ERR_UNSUPPORTED there).
  * out_dtype FP32 or BF16.
  * workspace: device, at least tpla_decode_workspace_size() bytes, 256-byte
- * aligned; its contents on entry do not matter.
+ * aligned; its contents on entry do not matter.  The split outputs go there
+ * (fp16 with a float scale per 64 columns on the streaming kernels, float32
+ * otherwise) and a second kernel on the same stream merges them into `out`.
  * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE, TPLA_ERR_DTYPE, TPLA_ERR_UNSUPPORTED
  * (no kernel for the shape, above), TPLA_ERR_WORKSPACE, TPLA_ERR_HIP.
  */
 tpla_status tpla_decode_shard(const tpla_decode_args* args, void* workspace,
                               size_t workspace_bytes, void* stream);
+
 
 /*
  * tpla_up_project: one device's value up-projection, optionally added into

@@ -22,7 +22,7 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtpla.so")
 
 SOURCES = ["tpla_api.hip", "hadamard.hip", "append.hip", "decode_generic.hip",
-           "decode_mfma.hip", "decode_latsplit.hip", "decode_mla.hip",
+           "decode_mfma.hip", "decode_latsplit.hip", "decode_roles.hip", "decode_mla.hip",
            "merge_combine.hip", "up_project.hip", "mla_prefill.hip"]
 
 # gfx950 only.  Packed fp32 vector ops are switched off for all device code.

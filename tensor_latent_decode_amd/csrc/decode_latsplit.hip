@@ -660,6 +660,7 @@ int decode_latsplit_heads_per_group(int heads, int d_s) {
 hipError_t launch_decode_latsplit(const DecodeParams& p, hipStream_t s) {
   if (!decode_latsplit_supported(p.heads, p.d_s, p.d_r, p.block_size)) return hipErrorNotSupported;
   if (decode_mla_supported(p.heads, p.d_s, p.d_r, p.block_size)) return launch_decode_mla(p, s);
+  if (decode_roles_supported(p.heads, p.d_s, p.d_r, p.block_size)) return launch_decode_roles(p, s);
   if (p.heads % 128 == 0 && p.d_s == 256) return launch_t<4, 256, 64, 3>(p, s);
   return launch_t<2, 128, 64, 2>(p, s);
 }

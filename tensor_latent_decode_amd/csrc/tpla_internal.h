@@ -165,6 +165,8 @@ int decode_latsplit_heads_per_group(int heads, int d_s);
 int decode_latsplit_max_chunk();   // tokens per split the latent-split kernel accepts
 int decode_latsplit_partial_block();   // columns per scale of its fp16 split outputs
 hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_roles(const DecodeParams& p, hipStream_t s);
+bool decode_roles_supported(int heads, int d_s, int d_r, int block_size);
 bool decode_mla_supported(int heads, int d_s, int d_r, int block_size);
 int decode_mla_max_chunk();
 int decode_mla_group_heads(int heads);   // heads per workgroup of the 512-wide kernel

@@ -28,7 +28,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, field, replace
-from typing import Optional, Tuple, Union
+from typing import List, Optional, Tuple, Union
 
 import numpy as np
 
@@ -154,7 +154,7 @@ def _unit_rms(x: np.ndarray) -> np.ndarray:
 
 
 def make_case(cfg: TplaConfig, *, batch: Optional[int] = None,
-              ctx: Optional[Union[int, Tuple[int, int]]] = None,
+              ctx: Optional[Union[int, Tuple[int, int], List[int]]] = None,
               seed: Optional[int] = None, block_size: Optional[int] = None,
               heads: Optional[int] = None) -> Case:
     """Draw one decode step's inputs for `cfg` (fields may be overridden)."""
@@ -178,6 +178,10 @@ def make_case(cfg: TplaConfig, *, batch: Optional[int] = None,
     if isinstance(cfg.ctx, tuple):
         lo, hi = cfg.ctx
         seq_lens = rngs[0].integers(lo, hi + 1, size=B).astype(np.int32)
+    elif isinstance(cfg.ctx, list):          # one length per sequence
+        if len(cfg.ctx) != B:
+            raise ValueError("a list of lengths needs one per sequence")
+        seq_lens = np.array(cfg.ctx, dtype=np.int32)
     else:
         seq_lens = np.full(B, int(cfg.ctx), dtype=np.int32)
     if np.any(seq_lens < 1):

@@ -405,6 +405,12 @@ def decode_workspace_size(args: DecodeArgs) -> int:
     return n.value
 
 
+def decode_workspace(args: DecodeArgs, device=None) -> torch.Tensor:
+    """A device workspace of the size tpla_decode_shard needs for `args`."""
+    need = decode_workspace_size(args)
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=device or "cuda")
+
+
 def decode_shard(q_latent: torch.Tensor, q_rope: Optional[torch.Tensor], cache: torch.Tensor,
                  block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
                  max_seq_len: int, out: Optional[torch.Tensor] = None,
@@ -418,9 +424,8 @@ def decode_shard(q_latent: torch.Tensor, q_rope: Optional[torch.Tensor], cache: 
         out = torch.empty((B, H, d_s), dtype=out_dtype, device=q_latent.device)
     args = make_decode_args(q_latent, q_rope, cache, block_table, seq_lens, scale, max_seq_len,
                             out, lse, num_splits)
-    need = decode_workspace_size(args)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_latent.device)
+        workspace = decode_workspace(args, q_latent.device)
     nbytes = workspace.numel() * workspace.element_size()
     _check("tpla_decode_shard", lib().tpla_decode_shard(ctypes.byref(args), workspace.data_ptr(),
                                                         nbytes, _stream(q_latent)))
