@@ -148,7 +148,7 @@ struct CopyJob {
   uint32_t lds;
 };
 
-template <int DS, int DR, bool kCopyS, int KPRE, int PPRE, int PRIO_S, int PRIO_V>
+template <int DS, int DR, bool kCopyS, int KPRE, int PPRE, int PRIO_S, int PRIO_V, int kPro>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   constexpr int HG = 128;                   // heads per workgroup
@@ -168,7 +168,8 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   static_assert(MPW == 2, "value waves own two latent tiles");
   static_assert(IPT <= NPF && IPT <= 2 * KS && 3 * IPT < 64, "copies per step");
   static_assert(kMaxTiles % (NS * 64) == 0, "tile table fill");
-  static_assert(KPRE >= 2 && KPRE <= 8 && PPRE >= 2 && PPRE <= 8, "prefetch depths");
+  static_assert(KPRE >= 2 && KPRE <= 12 && PPRE >= 2 && PPRE <= 8, "prefetch depths");
+  static_assert(kPro >= 1 && kPro <= 3, "tiles copied before the first barrier");
 
   __shared__ __attribute__((aligned(1024))) uint4 ktile[NB][SLOTS];
   __shared__ __attribute__((aligned(1024))) uint4 ptile[2][NPF * 64];
@@ -248,14 +249,17 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   // their columns into LDS (the K buffers, idle by then); then the whole
   // workgroup writes the group's rows, which are one contiguous block of the
   // workspace, with coalesced stores.
-  uint16_t* stage_h = reinterpret_cast<uint16_t*>(&ktile[0][0]);              // [HG][DS] fp16
-  float* stage_sc = reinterpret_cast<float*>(stage_h + HG * DS);                // [HG][DS / 64]
+  // Staged rows are DS + 8 halves apart: a value wave writes one row per
+  // lane pair, and rows a power-of-two apart would share their LDS banks.
+  constexpr int kStageRow = DS + 8;
+  uint16_t* stage_h = reinterpret_cast<uint16_t*>(&ktile[0][0]);              // [HG][kStageRow] fp16
+  float* stage_sc = reinterpret_cast<float*>(stage_h + HG * kStageRow);         // [HG][DS / 64]
   auto store_split_outputs = [&]() {
     barrier();                                      // the staged rows are complete
     const int64_t row0g = row0 + head0;
     uint64_t* dst = reinterpret_cast<uint64_t*>(reinterpret_cast<uint16_t*>(p.ws_o) + row0g * DS);
-    const uint64_t* src = reinterpret_cast<const uint64_t*>(stage_h);
-    for (int i = static_cast<int>(threadIdx.x); i < HG * DS / 4; i += 512) dst[i] = src[i];
+    for (int i = static_cast<int>(threadIdx.x); i < HG * DS / 4; i += 512)
+      dst[i] = *reinterpret_cast<const uint64_t*>(stage_h + (i / (DS / 4)) * kStageRow + (i % (DS / 4)) * 4);
     float* wsc = reinterpret_cast<float*>(reinterpret_cast<char*>(p.ws_o) +
                                           fp16_partials_scale_offset(p.num_splits, p.batch, p.heads, DS));
     for (int i = static_cast<int>(threadIdx.x); i < HG * (DS / 64); i += 512)
@@ -595,17 +599,23 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
       for (int ht = 0; ht < NS; ++ht)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[m][ht][r] = 0.f;
-#pragma unroll
-    for (int t = 0; t < 3; ++t) {
+    // Tiles 0 .. kPro-1 go out before the first barrier, the rest of the
+    // first three after it: every CU starts at once, and the copies the
+    // memory system holds when tile 0 is wanted delay it.
+    auto copy_tile = [&](int t) {
       const uint32_t row64 = first ? (t < ntiles ? tile_row(t, pg[t]) : 0u)
                                    : __builtin_amdgcn_readfirstlane(trow[min(t, ntiles - 1)]);
       const CopyJob j = make_job(t, t, row64, ntiles, t1);
 #pragma unroll
       for (int ci = 0; ci < IPT; ++ci) copy_chunk(j, src_off, lq, ci);
-    }
-    first = false;
-    wait_vm<2 * IPT>();                           // tile 0
+    };
+#pragma unroll
+    for (int t = 0; t < kPro; ++t) copy_tile(t);
+    wait_vm<(kPro - 1) * IPT>();                  // tile 0
     barrier();                                    // B_a
+#pragma unroll
+    for (int t = kPro; t < 3; ++t) copy_tile(t);
+    first = false;
 #pragma unroll
     for (int k = 0; k < 8; ++k) vc[k >> 2][k & 3] = rd_v(reinterpret_cast<const char*>(&ktile[0][0]), k >> 2, k & 3);
     wait_vm<IPT>();                               // tile 1
@@ -650,7 +660,7 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     amax = both_halves_max(amax);
     const float hs = amax > 0.f ? 1.0f / amax : 0.f;
     const int hrow = ht * 32 + l31;
-    uint16_t* dst = stage_h + hrow * DS + 64 * lq + 4 * half;
+    uint16_t* dst = stage_h + hrow * kStageRow + 64 * lq + 4 * half;
 #pragma unroll
     for (int mm = 0; mm < MPW; ++mm)
 #pragma unroll
@@ -674,6 +684,7 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
 // visible in one place).
 constexpr bool kRolesCopyS = false;
 constexpr int kRolesKPre = 4, kRolesPPre = 3, kRolesPrioS = 0, kRolesPrioV = 0;
+constexpr int kRolesPro = 3;
 
 }  // namespace
 
@@ -687,7 +698,7 @@ hipError_t launch_decode_roles(const DecodeParams& p, hipStream_t s) {
   const int n_units = p.num_splits * p.batch * (p.heads / 128);
   const int per_xcd = (n_units + 7) / 8;
   hipLaunchKernelGGL((decode_roles_kernel<256, 64, kRolesCopyS, kRolesKPre, kRolesPPre, kRolesPrioS,
-                                         kRolesPrioV>),
+                                         kRolesPrioV, kRolesPro>),
                      dim3(8 * per_xcd), dim3(512), 0, s, p, n_units, per_xcd);
   return hipGetLastError();
 }
