@@ -308,6 +308,28 @@ tpla_status tpla_decode_suggest_splits(const tpla_decode_args* args, const int32
 tpla_status tpla_decode_shard(const tpla_decode_args* args, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/*
+ * tpla_decode_shard_noalloc: tpla_decode_shard without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * split outputs go to a static device array of the library,
+ * tpla_decode_noalloc_scratch_bytes() bytes (64 MiB) on every device it
+ * runs on, held until the process ends; the call allocates nothing.  The
+ * first call on a device looks up that device's copy
+ * (hipGetSymbolAddress) with the device current, so make the stream's
+ * device the current one.  Same kernels, same results as tpla_decode_shard
+ * with a workspace.  Nothing in the scratch needs to start at zero.
+ * Calls that overlap on one device (other streams, other threads) share the
+ * one array and race: order them on one stream or serialise them.
+ * Errors: as tpla_decode_shard; TPLA_ERR_WORKSPACE when the call's split
+ * outputs (tpla_decode_workspace_size) exceed the scratch;
+ * TPLA_ERR_UNSUPPORTED for a device index of 64 or more.
+ */
+tpla_status tpla_decode_shard_noalloc(const tpla_decode_args* args, void* stream);
+
+/* tpla_decode_noalloc_scratch_bytes: size of that static scratch, bytes. */
+size_t tpla_decode_noalloc_scratch_bytes(void);
+
 
 /*
  * tpla_up_project: one device's value up-projection, optionally added into

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "tpla.h"
@@ -393,18 +394,20 @@ tpla_status tpla_decode_workspace_size(const tpla_decode_args* args, size_t* byt
   return ok();
 }
 
-tpla_status tpla_decode_shard(const tpla_decode_args* a, void* workspace, size_t workspace_bytes,
-                              void* stream) {
-  tpla_status st = check_decode(a);
-  if (st != TPLA_OK) return st;
-  Plan pl;
-  st = plan_decode(a, &pl);
-  if (st != TPLA_OK) return st;
-  if (workspace == nullptr || workspace_bytes < pl.ws_bytes)
-    return fail(TPLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", pl.ws_bytes,
-                workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(TPLA_ERR_ALIGN, "workspace must be 256-byte aligned");
+}  // extern "C"
+
+// Scratch of tpla_decode_shard_noalloc: one copy per device, held until the
+// process ends.  Host code uses only the address hipGetSymbolAddress gives
+// for the current device (the array's name is a host-side stand-in).
+constexpr size_t kNoAllocScratchBytes = size_t{64} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// The decode and merge launches of a checked, planned call whose split
+// outputs go to `workspace` (at least pl.ws_bytes, 256-byte aligned).
+tpla_status launch_planned_decode(const tpla_decode_args* a, const Plan& pl, void* workspace,
+                                  void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   tpla::DecodeParams p{};
@@ -457,6 +460,68 @@ tpla_status tpla_decode_shard(const tpla_decode_args* a, void* workspace, size_t
   m.lse = a->lse;
   return hip_status(tpla::launch_merge(m, s), "merge launch");
 }
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device.
+tpla_status scratch_address(void** ptr_out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(TPLA_ERR_UNSUPPORTED, "device %d is past the %d devices the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(TPLA_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *ptr_out = g_scratch_ptr[dev];
+  return TPLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tpla_status tpla_decode_shard(const tpla_decode_args* a, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  tpla_status st = check_decode(a);
+  if (st != TPLA_OK) return st;
+  Plan pl;
+  st = plan_decode(a, &pl);
+  if (st != TPLA_OK) return st;
+  if (workspace == nullptr || workspace_bytes < pl.ws_bytes)
+    return fail(TPLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", pl.ws_bytes,
+                workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(TPLA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  return launch_planned_decode(a, pl, workspace, stream);
+}
+
+tpla_status tpla_decode_shard_noalloc(const tpla_decode_args* a, void* stream) {
+  tpla_status st = check_decode(a);
+  if (st != TPLA_OK) return st;
+  Plan pl;
+  st = plan_decode(a, &pl);
+  if (st != TPLA_OK) return st;
+  if (pl.ws_bytes > kNoAllocScratchBytes)
+    return fail(TPLA_ERR_WORKSPACE,
+                "this call needs %zu bytes of split outputs; the library's static scratch holds %zu "
+                "(fewer splits, sequences or heads per call fit)",
+                pl.ws_bytes, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != TPLA_OK) return st;
+  return launch_planned_decode(a, pl, ws, stream);
+}
+
+size_t tpla_decode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 tpla_status tpla_mla_prefill(const tpla_prefill_args* a, void* stream) {
   if (a == nullptr) return fail(TPLA_ERR_NULL, "args is NULL");

@@ -111,6 +111,9 @@ def lib() -> ctypes.CDLL:
                                  vp, i64, dt, vp]
     L.tpla_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(sz)]
     L.tpla_decode_shard.argtypes = [ctypes.POINTER(DecodeArgs), vp, sz, vp]
+    L.tpla_decode_shard_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), vp]
+    L.tpla_decode_noalloc_scratch_bytes.argtypes = []
+    L.tpla_decode_noalloc_scratch_bytes.restype = sz
     L.tpla_combine_shards.argtypes = [ctypes.POINTER(vp), dt, i32, i32, i32, i32, vp, dt, i32, vp]
     L.tpla_rotate_append.argtypes = [ctypes.POINTER(RotateAppendArgs), vp]
     L.tpla_decode_suggest_splits.argtypes = [ctypes.POINTER(DecodeArgs), vp, ctypes.POINTER(i32)]
@@ -118,7 +121,7 @@ def lib() -> ctypes.CDLL:
                                   i32, i32, i32, i32, i32, vp]
     L.tpla_mla_prefill.argtypes = [ctypes.POINTER(PrefillArgs), vp]
     for f in ("tpla_hadamard_latent", "tpla_append_kv", "tpla_decode_workspace_size",
-              "tpla_decode_shard", "tpla_combine_shards", "tpla_rotate_append",
+              "tpla_decode_shard", "tpla_decode_shard_noalloc", "tpla_combine_shards", "tpla_rotate_append",
               "tpla_decode_suggest_splits", "tpla_up_project", "tpla_mla_prefill"):
         getattr(L, f).restype = ctypes.c_int
     L.tpla_status_string.argtypes = [ctypes.c_int]
@@ -430,6 +433,24 @@ def decode_shard(q_latent: torch.Tensor, q_rope: Optional[torch.Tensor], cache: 
     _check("tpla_decode_shard", lib().tpla_decode_shard(ctypes.byref(args), workspace.data_ptr(),
                                                         nbytes, _stream(q_latent)))
     return out, lse
+
+
+def decode_shard_noalloc(q_latent: torch.Tensor, q_rope: Optional[torch.Tensor],
+                         cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                         scale: float, max_seq_len: int, out: torch.Tensor,
+                         lse: Optional[torch.Tensor] = None, num_splits: int = 0):
+    """decode_shard through tpla_decode_shard_noalloc: the library's static device
+    scratch holds the split outputs, and nothing is allocated (so `out` is required)."""
+    _gpu(q_latent, q_rope, cache, block_table, seq_lens, out, lse)
+    args = make_decode_args(q_latent, q_rope, cache, block_table, seq_lens, scale, max_seq_len,
+                            out, lse, num_splits)
+    _check("tpla_decode_shard_noalloc",
+           lib().tpla_decode_shard_noalloc(ctypes.byref(args), _stream(q_latent)))
+    return out, lse
+
+
+def decode_noalloc_scratch_bytes() -> int:
+    return int(lib().tpla_decode_noalloc_scratch_bytes())
 
 
 def make_prefill_args(q_latent: torch.Tensor, q_rope: torch.Tensor, kv: torch.Tensor,

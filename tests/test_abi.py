@@ -176,6 +176,22 @@ def test_decode_null_args_and_workspace_checks():
     _fails(L.tpla_decode_shard(ctypes.byref(_args()), FAKE + 4, 1 << 30, None), 3)
 
 
+def test_decode_noalloc_checks_before_touching_the_device():
+    # every rejection here happens on the host, before any device query
+    L = tpla.lib()
+    cap = tpla.decode_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    _fails(L.tpla_decode_shard_noalloc(None, None), 1)
+    _fails(L.tpla_decode_shard_noalloc(ctypes.byref(_args(batch=0)), None), 2)
+    # 64 sequences x 128 heads x 16 splits of float32 split outputs pass 64 MiB
+    big = _args(batch=64, num_splits=16)
+    n = ctypes.c_size_t()
+    assert L.tpla_decode_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0
+    assert n.value > cap
+    _fails(L.tpla_decode_shard_noalloc(ctypes.byref(big), None), 6)
+    assert b"static scratch" in L.tpla_last_error()
+
+
 def test_combine_argument_checks():
     L = tpla.lib()
     ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
