@@ -6,8 +6,10 @@
 // latent slice; the softmax is the shard's own (TPLA abstract; edgentiq
 // blog, "How TPLA Works: Smart Slicing and Reparameterization").
 //
-// One workgroup of eight waves per (token split, sequence, 128 heads), one
-// workgroup per CU, two waves per SIMD.  The waves take two roles:
+// One workgroup of eight waves per (work unit, 128 heads), one workgroup
+// per CU, two waves per SIMD.  A work unit is a token range of one sequence
+// from the unit map of the lengths (unit_map.h): about one per CU, equal in
+// tiles whatever the mix of lengths.  The waves take two roles:
 //
 //   score waves 0..3   wave h owns heads 32h .. 32h+31:
 //                      S^T[token, head] = K_tile . Q^T over d_s + d_r, then
@@ -44,6 +46,7 @@
 #include <type_traits>
 
 #include "tpla_internal.h"
+#include "unit_map.h"
 
 namespace tpla {
 namespace {
@@ -65,7 +68,7 @@ constexpr kTrue_t kTrue{};
 constexpr kFalse_t kFalse{};
 
 constexpr int kTile = 64;
-constexpr int kMaxTiles = 1024;     // tiles per split (the host plans splits to fit)
+constexpr int kMaxTiles = 1024;     // tiles per unit (the LDS tile table; the unit map caps units)
 constexpr float kRescaleSum = 0x1p64f;   // row sum that makes a split run again
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -178,16 +181,17 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   __shared__ int flags[NS];
   __shared__ int pcount;                 // tiles whose P^T fragments 2, 3 are in LDS (x NS)
 
-  // ---- work unit (XCD-aware) ----
+  // ---- work unit ----
+  // Launch slot n -> unit u (XCD-aware: consecutive units, the head groups
+  // and token ranges of one sequence, share an XCD and its L2); u -> head
+  // group and sequence unit su; su -> (sequence, tokens) from the unit map
+  // of the lengths, which workgroup 0 also writes out for the merge.
   const int n = blockIdx.x;
   const int u = (n & 7) * units_per_xcd + (n >> 3);
   if (u >= n_units) return;
-  const int S = p.num_splits;
   const int HGS = p.heads / HG;
-  const int split = u % S;
-  const int bh = u / S;
-  const int hg = bh % HGS;
-  const int b = bh / HGS;
+  const int hg = u % HGS;
+  const int su = u / HGS;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -195,10 +199,15 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   const int head0 = hg * HG;
   const bool is_score = wave < NS;
 
+  WorkUnit wu;
+  if (!find_unit(p, su, kMaxTiles, (n == 0 && wave == NS) ? p.unit_table : nullptr, &wu)) return;
+  const int b = wu.b;
+  const int t0 = wu.t0;
+  const int t1 = wu.t1;                     // t0 < t1: a unit has tokens
+  const int ntiles = (t1 - t0 + kTile - 1) / kTile;
   const int32_t* bt_row = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
   const int bs = p.block_size;
-  const int t0 = split * p.chunk;
-  const int64_t row0 = (static_cast<int64_t>(split) * p.batch + b) * p.heads;
+  const int64_t row0 = static_cast<int64_t>(su) * p.heads;
   const uint16_t* cache = static_cast<const uint16_t*>(p.cache);
 
   // The softmax takes a tile's max before scaling, which needs a positive
@@ -217,7 +226,6 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
                     static_cast<uint32_t>((tb % bs) / kTile)
               : 0u;
   };
-  auto clamp_len = [&](int L) { return max(0, min(L, min(p.max_seq_len, p.max_blocks * p.block_size))); };
   // Source offsets of this lane's chunks when it is copying wave cw.
   auto copy_offsets = [&](int cw, uint32_t (&so)[IPT]) {
 #pragma unroll
@@ -261,7 +269,7 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     for (int i = static_cast<int>(threadIdx.x); i < HG * DS / 4; i += 512)
       dst[i] = *reinterpret_cast<const uint64_t*>(stage_h + (i / (DS / 4)) * kStageRow + (i % (DS / 4)) * 4);
     float* wsc = reinterpret_cast<float*>(reinterpret_cast<char*>(p.ws_o) +
-                                          fp16_partials_scale_offset(p.num_splits, p.batch, p.heads, DS));
+                                          fp16_partials_scale_offset(p.max_units, 1, p.heads, DS));
     for (int i = static_cast<int>(threadIdx.x); i < HG * (DS / 64); i += 512)
       wsc[row0g * (DS / 64) + i] = stage_sc[i];
   };
@@ -273,9 +281,9 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     if constexpr (PRIO_S > 0) __builtin_amdgcn_s_setprio(PRIO_S);
     const int ht = wave;
     const int head = head0 + ht * 32 + l31;
-    // First memory round trip: the query fragments (B operand of S^T), the
-    // block ids of every tile the split may cover (for the tile table) and
-    // the sequence length.
+    // First memory round trip after the unit map: the query fragments (B
+    // operand of S^T) and the block ids of the unit's tiles (for the tile
+    // table).
     bf16x8_t qf[KS];
     {
       const uint16_t* ql = static_cast<const uint16_t*>(p.q_latent) + b * p.qls_b + head * p.qls_h;
@@ -287,26 +295,16 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
       }
     }
     constexpr int kFill = kMaxTiles / (NS * 64);
-    const int ctiles = p.chunk / kTile;
     int fpg[kFill];
 #pragma unroll
     for (int k = 0; k < kFill; ++k) {
       const int t = k * NS * 64 + static_cast<int>(threadIdx.x);
-      fpg[k] = t < ctiles ? bt_row[min((t0 + t * kTile) / bs, p.max_blocks - 1)] : 0;
+      fpg[k] = t < ntiles ? bt_row[min((t0 + t * kTile) / bs, p.max_blocks - 1)] : 0;
     }
-    int L = scalar_load(p.seq_lens + b);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) asm volatile("" : : "v"(qf[kk]));
 #pragma unroll
     for (int k = 0; k < kFill; ++k) asm volatile("" : : "v"(fpg[k]));
-    asm volatile("" : : "s"(L));
-    L = clamp_len(L);
-    const int t1 = min(L, t0 + p.chunk);
-    if (t0 >= t1) {                             // no tokens in this split
-      if (half == 0) p.ws_lse[row0 + head] = -INFINITY;
-      return;
-    }
-    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
     const int nfull = (t1 - t0) / kTile;
     if (p.scale_log2 < 0.f) {
 #pragma unroll
@@ -507,12 +505,7 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
 #pragma unroll
   for (int t = 0; t < 3; ++t)
     pg[t] = scalar_load(bt_row + min((t0 + t * kTile) / bs, p.max_blocks - 1));
-  int L = scalar_load(p.seq_lens + b);
-  asm volatile("" : : "s"(pg[0]), "s"(pg[1]), "s"(pg[2]), "s"(L));
-  L = clamp_len(L);
-  const int t1 = min(L, t0 + p.chunk);
-  if (t0 >= t1) return;                         // no tokens in this split
-  const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+  asm volatile("" : : "s"(pg[0]), "s"(pg[1]), "s"(pg[2]));
   uint32_t src_off[IPT];
   copy_offsets(lq, src_off);
 
@@ -688,14 +681,18 @@ constexpr int kRolesPro = 3;
 
 }  // namespace
 
+int decode_roles_max_tiles() { return kMaxTiles; }
+
 bool decode_roles_supported(int heads, int d_s, int d_r, int block_size) {
   return heads % 128 == 0 && d_s == 256 && d_r == 64 && block_size % kTile == 0;
 }
 
 hipError_t launch_decode_roles(const DecodeParams& p, hipStream_t s) {
   if (!decode_roles_supported(p.heads, p.d_s, p.d_r, p.block_size)) return hipErrorNotSupported;
-  if (p.chunk > kMaxTiles * kTile || p.chunk % kTile != 0) return hipErrorInvalidValue;
-  const int n_units = p.num_splits * p.batch * (p.heads / 128);
+  if (p.chunk > kMaxTiles * kTile || p.chunk % kTile != 0 || p.max_units < 1 ||
+      (p.unit_target == 0 && p.chunk < kTile) || p.unit_table == nullptr)
+    return hipErrorInvalidValue;
+  const int n_units = p.max_units * (p.heads / 128);
   const int per_xcd = (n_units + 7) / 8;
   hipLaunchKernelGGL((decode_roles_kernel<256, 64, kRolesCopyS, kRolesKPre, kRolesPPre, kRolesPrioS,
                                          kRolesPrioV, kRolesPro>),

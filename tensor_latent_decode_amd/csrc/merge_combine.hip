@@ -127,7 +127,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_ite
 // fp16 split outputs (streaming kernels; d_s a multiple of blk_cols, which
 // is a multiple of 8): one thread per (b, h, 8 consecutive columns), so a
 // wavefront reads two whole 256-column rows of a split with 16-byte loads.
-// Up to 16 splits per memory round trip, as above.
+// Up to 16 splits per memory round trip, as above.  The splits of sequence
+// b are either rows (s, b, h) for s < splits, or (unit table) rows
+// (first_b + s, h) for s < n_b.
 template <bool kBf16Out>
 __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_items, int per_xcd) {
   const int n = blockIdx.x;
@@ -138,19 +140,27 @@ __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_i
   const int64_t bh = item / o8;
   const int col = static_cast<int>(item % o8) * 8;
   const int nblk = p.d_s / p.blk_cols;
-  const int64_t stride_s = static_cast<int64_t>(p.batch) * p.heads;
+  const int b = static_cast<int>(bh / p.heads);
+  const int h = static_cast<int>(bh % p.heads);
+  const bool units = p.unit_table != nullptr;
+  const int2 ut = units ? reinterpret_cast<const int2*>(p.unit_table)[b] : make_int2(0, p.splits);
+  const int nsplit = ut.y;
+  // row of split s: a unit row, or the (split, sequence) row
+  const int64_t row_base = units ? static_cast<int64_t>(ut.x) * p.heads + h : bh;
+  const int64_t row_step = units ? p.heads : static_cast<int64_t>(p.batch) * p.heads;
   const uint16_t* wh = reinterpret_cast<const uint16_t*>(p.ws_o);
-  const float* wsc = reinterpret_cast<const float*>(reinterpret_cast<const char*>(p.ws_o) +
-                                                    fp16_partials_scale_offset(p.splits, p.batch, p.heads, p.d_s));
+  const float* wsc = reinterpret_cast<const float*>(
+      reinterpret_cast<const char*>(p.ws_o) +
+      fp16_partials_scale_offset(p.splits, units ? 1 : p.batch, p.heads, p.d_s));
   constexpr int kC = 16;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, tot = 0.f;
-  for (int s0 = 0; s0 < p.splits; s0 += kC) {
+  for (int s0 = 0; s0 < nsplit; s0 += kC) {
     float l[kC], f[kC];
     uint4 v[kC];
 #pragma unroll
     for (int u = 0; u < kC; ++u) {
-      const int64_t row = static_cast<int64_t>(min(s0 + u, p.splits - 1)) * stride_s + bh;
+      const int64_t row = row_base + static_cast<int64_t>(min(s0 + u, nsplit - 1)) * row_step;
       l[u] = p.ws_lse[row];
       f[u] = wsc[row * nblk + col / p.blk_cols];
       v[u] = *reinterpret_cast<const uint4*>(wh + row * p.d_s + col);
@@ -158,7 +168,7 @@ __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_i
     float cm = m;
 #pragma unroll
     for (int u = 0; u < kC; ++u) {
-      if (s0 + u >= p.splits) l[u] = -INFINITY;
+      if (s0 + u >= nsplit) l[u] = -INFINITY;
       cm = fmaxf(cm, l[u]);
     }
     if (cm == -INFINITY) continue;              // no tokens so far
@@ -188,8 +198,6 @@ __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_i
     for (int i = 0; i < 8; ++i) acc[i] *= inv;
     lse = m + __logf(tot);
   }
-  const int b = static_cast<int>(bh / p.heads);
-  const int h = static_cast<int>(bh % p.heads);
   const int64_t obase = b * p.out_sb + h * p.out_sh + col;
   if constexpr (kBf16Out) {
     uint16_t* o = static_cast<uint16_t*>(p.out) + obase;
@@ -272,6 +280,7 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
                          items, static_cast<int>(per_xcd));
     return hipGetLastError();
   }
+  if (p.unit_table != nullptr) return hipErrorInvalidValue;   // unit rows come as fp16 only
   const int64_t n_items = static_cast<int64_t>(p.batch) * p.heads * ((p.d_s + 3) / 4);
   const int64_t wgs = (n_items + 255) / 256;
   const int64_t per_xcd = (wgs + 7) / 8;

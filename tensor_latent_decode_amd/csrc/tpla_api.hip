@@ -126,15 +126,23 @@ tpla_status check_decode(const tpla_decode_args* a) {
 struct Plan {
   int splits;
   int chunk;
+  // The roles kernel cuts the work into units on the device (unit_map.h):
+  // automatic calls target one unit per CU, explicit ones take `chunk`.
+  bool units;
+  int unit_target;
+  int max_units;
   size_t ws_o_bytes;
+  size_t table_off;      // unit table [batch][2] int32 (units only)
   size_t ws_bytes;
 };
+
+size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 tpla_status plan_decode(const tpla_decode_args* a, Plan* pl) {
   const int maxlen = a->max_seq_len;
   int want = a->num_splits;
+  int cus = 0;
   if (want == 0) {
-    int cus = 0;
     const tpla_status st = device_cus(&cus);
     if (st != TPLA_OK) return st;
     int64_t groups = a->batch;
@@ -163,9 +171,27 @@ tpla_status plan_decode(const tpla_decode_args* a, Plan* pl) {
   const int tiles_per = (max_tiles + want - 1) / want;
   pl->chunk = tiles_per * 64;
   pl->splits = std::max(1, (maxlen + pl->chunk - 1) / pl->chunk);
-  const size_t rows = static_cast<size_t>(pl->splits) * a->batch * a->heads;
-  pl->ws_o_bytes = (rows * a->d_s * sizeof(float) + 255) & ~static_cast<size_t>(255);
-  pl->ws_bytes = pl->ws_o_bytes + ((rows * sizeof(float) + 255) & ~static_cast<size_t>(255));
+  pl->units = decode_path(a) == Path::kStream &&
+              tpla::decode_roles_supported(a->heads, a->d_s, a->d_r, a->block_size);
+  pl->unit_target = 0;
+  pl->max_units = 0;
+  size_t rows = static_cast<size_t>(pl->splits) * a->batch * a->heads;
+  if (pl->units) {
+    const int cap = tpla::decode_roles_max_tiles();
+    if (a->num_splits == 0) {
+      // one unit per CU; more only where a sequence needs more than the
+      // largest unit's tiles (or the batch has more sequences than CUs)
+      pl->unit_target = std::max(1, cus / (a->heads / 128));
+      pl->max_units = std::max<int64_t>(
+          pl->unit_target, static_cast<int64_t>(a->batch) * ((max_tiles + cap - 1) / cap));
+    } else {
+      pl->max_units = pl->splits * a->batch;
+    }
+    rows = static_cast<size_t>(pl->max_units) * a->heads;
+  }
+  pl->ws_o_bytes = round256(rows * a->d_s * sizeof(float));
+  pl->table_off = pl->ws_o_bytes + round256(rows * sizeof(float));
+  pl->ws_bytes = pl->table_off + (pl->units ? round256(static_cast<size_t>(a->batch) * 8) : 0);
   return TPLA_OK;
 }
 
@@ -216,6 +242,11 @@ tpla_status tpla_decode_suggest_splits(const tpla_decode_args* args, const int32
   if (st != TPLA_OK) return st;
   if (decode_path(&a) != Path::kStream) {
     *num_splits = pl.splits;
+    return ok();
+  }
+  if (pl.units) {
+    // the automatic plan balances units over the lengths on the device
+    *num_splits = 0;
     return ok();
   }
   int cus = 0;
@@ -433,6 +464,10 @@ tpla_status launch_planned_decode(const tpla_decode_args* a, const Plan& pl, voi
   p.seq_lens = a->seq_lens;
   p.ws_o = static_cast<float*>(workspace);
   p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_o_bytes);
+  p.unit_target = pl.unit_target;
+  p.max_units = pl.max_units;
+  p.unit_table = pl.units ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + pl.table_off)
+                          : nullptr;
 
   hipError_t e;
   switch (decode_path(a)) {
@@ -443,7 +478,8 @@ tpla_status launch_planned_decode(const tpla_decode_args* a, const Plan& pl, voi
   if (e != hipSuccess) return hip_status(e, "decode launch");
 
   tpla::MergeParams m{};
-  m.splits = pl.splits;
+  m.splits = pl.units ? pl.max_units : pl.splits;
+  m.unit_table = p.unit_table;
   m.batch = a->batch;
   m.heads = a->heads;
   m.d_s = a->d_s;

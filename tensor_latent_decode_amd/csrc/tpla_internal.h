@@ -53,6 +53,13 @@ struct DecodeParams {
   const int32_t* seq_lens;
   float* ws_o;                  // [splits, batch, heads, d_s]
   float* ws_lse;                // [splits, batch, heads]
+  // Kernels that cut the work into units themselves (unit_map.h) ignore
+  // num_splits: their split outputs are rows [unit, heads], at most
+  // max_units units, and unit_table receives each sequence's units.
+  int unit_target;              // > 0: units of one chunk size chosen so about this many exist;
+                                // 0: chunk = `chunk`
+  int max_units;                // bound on the units of this call (launch size, workspace rows)
+  int32_t* unit_table;          // [batch][2]: first unit, unit count
 };
 
 // Split outputs are either float32 [splits, batch, heads, d_s] at ws_o, or
@@ -67,6 +74,10 @@ __host__ __device__ inline size_t fp16_partials_scale_offset(int splits, int bat
 struct MergeParams {
   int splits, batch, heads, d_s;
   int blk_cols;                 // 0: float32 partials; else fp16 partials, scale per blk_cols
+  // Non-null: the split outputs are rows [unit, heads] of `splits` units
+  // (batch 1 in the scale offset) and sequence b owns units
+  // unit_table[2b] .. unit_table[2b] + unit_table[2b+1] - 1.
+  const int32_t* unit_table;
   const float* ws_o;
   const float* ws_lse;
   void* out;
@@ -167,6 +178,7 @@ int decode_latsplit_partial_block();   // columns per scale of its fp16 split ou
 hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_roles(const DecodeParams& p, hipStream_t s);
 bool decode_roles_supported(int heads, int d_s, int d_r, int block_size);
+int decode_roles_max_tiles();      // 64-token tiles one unit of the roles kernel may hold
 bool decode_mla_supported(int heads, int d_s, int d_r, int block_size);
 int decode_mla_max_chunk();
 int decode_mla_group_heads(int heads);   // heads per workgroup of the 512-wide kernel

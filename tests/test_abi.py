@@ -142,10 +142,15 @@ def test_decode_workspace_size_with_fixed_splits():
     rows = 4 * 2 * 128
     o = (rows * 256 * 4 + 255) // 256 * 256
     lse = (rows * 4 + 255) // 256 * 256
-    assert n.value == o + lse
+    table = 256                       # the roles kernel's unit table, [batch][2] int32
+    assert n.value == o + lse + table
     # more splits than tiles are clamped to one per 64-token tile
     assert L.tpla_decode_workspace_size(ctypes.byref(_args(num_splits=1000)), ctypes.byref(n)) == 0
-    assert n.value == (50 * 2 * 128 * 256 * 4 + 255) // 256 * 256 + (50 * 2 * 128 * 4 + 255) // 256 * 256
+    assert n.value == ((50 * 2 * 128 * 256 * 4 + 255) // 256 * 256 + (50 * 2 * 128 * 4 + 255) // 256 * 256
+                       + table)
+    # the float32 kernel: split outputs only
+    assert L.tpla_decode_workspace_size(ctypes.byref(_args(dtype=0)), ctypes.byref(n)) == 0
+    assert n.value == o + lse
 
 
 @pytest.mark.parametrize("kw,code", [

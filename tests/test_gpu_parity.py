@@ -479,8 +479,10 @@ def test_decode_zero_and_negative_scale(shape, scale):
 
 def test_suggested_splits_uniform_and_ragged():
     """The host-side split suggestion keeps the automatic count for uniform
-    32K lengths (DeepSeek-V3 and Kimi-K2 shards), and a ragged batch decoded
-    with its suggestion matches the oracle."""
+    32K lengths (DeepSeek-V3 and Kimi-K2 shards); for the DeepSeek-V3 shard,
+    whose kernel balances units over the lengths itself, it is the automatic
+    plan (0); a ragged batch decoded with its suggestion matches the oracle
+    on both shapes."""
     for heads, d_s in ((128, 256), (64, 128)):
         a = tpla.DecodeArgs()          # sizes only: the call reads no device memory
         a.batch, a.heads, a.d_s, a.d_r = 16, heads, d_s, 64
@@ -494,22 +496,104 @@ def test_suggested_splits_uniform_and_ragged():
         auto = tpla.decode_workspace_size(a)
         a.num_splits = tpla.decode_suggest_splits(a, np.full(16, 32768, np.int32))
         assert tpla.decode_workspace_size(a) == auto, (heads, a.num_splits)
-    case = make_case(CONFIGS["ragged_tp2"], batch=8, ctx=(64, 6000), seed=33)
+    for name in ("ragged_tp2", "kimi_k2_32k"):
+        case = make_case(CONFIGS[name], batch=8, ctx=(64, 6000), seed=33)
+        gc = GpuCase(case)
+        d_s = case.cfg.d_s
+        cache = gc.prefill(0, d_s)
+        maxlen = int(case.seq_lens.max())
+        out = torch.empty((case.cfg.batch, case.cfg.heads, d_s), dtype=torch.float32, device="cuda")
+        args = tpla.make_decode_args(gc.q_latent[:, :, :d_s], gc.q_rope, cache, gc.bt, gc.hist_lens,
+                                     case.cfg.scale, maxlen, out)
+        sugg = tpla.decode_suggest_splits(args, case.seq_lens - 1)
+        if name == "ragged_tp2":
+            assert sugg == 0
+        else:
+            assert 1 <= sugg <= (maxlen + 63) // 64
+        o, _ = tpla.decode_shard(gc.q_latent[:, :, :d_s], gc.q_rope, cache, gc.bt, gc.hist_lens,
+                                 case.cfg.scale, maxlen, num_splits=sugg)
+        torch.cuda.synchronize()
+        for b in range(case.cfg.batch):
+            _, parts = oracle_step(case, b, case.cfg.tp, hadamard=False, with_new=False,
+                                   q_is_rotated=True)
+            assert rel_err(host_f64(o)[b], parts[0][0]) <= TOL_BF16, (name, b)
+
+
+def unit_map_reference(lens, n_target, max_tiles, cap):
+    """The work units the balanced plan specifies, by brute force: T_b tiles
+    per sequence, the smallest chunk c (tiles) with sum ceil(T_b / c) <= n_target
+    (else the largest unit), and (first unit, unit count) per sequence."""
+    tiles = [(min(max(int(L), 0), cap) + 63) // 64 for L in lens]
+    nonempty = sum(t > 0 for t in tiles)
+    if sum(tiles) == 0:
+        c = 1
+    elif nonempty >= n_target:
+        c = max_tiles
+    else:
+        c = next((c for c in range(1, max_tiles + 1)
+                  if sum(-(-t // c) for t in tiles) <= n_target), max_tiles)
+    counts = [-(-t // c) for t in tiles]
+    firsts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64)
+    return c, np.stack([firsts, np.array(counts, dtype=np.int64)], axis=1)
+
+
+def balanced_shard_decode(case, g=0):
+    """Shard g's decode with the automatic (balanced-unit) plan; returns
+    (out, lse, unit table read back from the workspace's tail)."""
     gc = GpuCase(case)
-    d_s = case.cfg.d_s
-    cache = gc.prefill(0, d_s)
+    cfg = case.cfg
+    B, H, d_s = cfg.batch, cfg.heads, cfg.d_s
+    q = tpla.hadamard_latent(gc.q_latent)
+    new = tpla.hadamard_latent(gc.new_latent)
+    cache = gc.prefill(g, d_s)
+    tpla.append_kv(cache, gc.bt, gc.new_seq, gc.new_pos, new[:, g * d_s:(g + 1) * d_s], gc.new_rope)
+    qs = q[:, :, g * d_s:(g + 1) * d_s]
+    out = torch.full((B, H, d_s), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
     maxlen = int(case.seq_lens.max())
-    out = torch.empty((case.cfg.batch, case.cfg.heads, d_s), dtype=torch.float32, device="cuda")
-    args = tpla.make_decode_args(gc.q_latent[:, :, :d_s], gc.q_rope, cache, gc.bt, gc.hist_lens,
-                                 case.cfg.scale, maxlen, out)
-    sugg = tpla.decode_suggest_splits(args, case.seq_lens - 1)
-    assert 1 <= sugg <= (maxlen + 63) // 64
-    o, _ = tpla.decode_shard(gc.q_latent[:, :, :d_s], gc.q_rope, cache, gc.bt, gc.hist_lens,
-                             case.cfg.scale, maxlen, num_splits=sugg)
+    args = tpla.make_decode_args(qs, gc.q_rope, cache, gc.bt, gc.seq_lens, cfg.scale, maxlen, out,
+                                 lse, 0)
+    ws = tpla.decode_workspace(args)
+    tpla.decode_shard(qs, gc.q_rope, cache, gc.bt, gc.seq_lens, cfg.scale, maxlen, out=out, lse=lse,
+                      workspace=ws)
     torch.cuda.synchronize()
+    tail = (B * 8 + 255) // 256 * 256
+    table = ws[ws.numel() - tail:ws.numel() - tail + B * 8].cpu().numpy().view(np.int32).reshape(B, 2)
+    return out.cpu().numpy(), lse.cpu().numpy(), table
+
+
+def _balanced_lens(kind):
+    rng = np.random.default_rng(123)
+    if kind == "c5_mix":
+        return rng.integers(1024, 32769, size=32).tolist()
+    if kind == "min_max":
+        # one token, tile edges, and one sequence past the largest unit (1024 tiles)
+        return [1, 64, 65, 70001, 2049, 1]
+    if kind == "more_than_cus":
+        # more sequences than CUs: one unit each, the long one two
+        return [70001] + rng.integers(1, 300, size=299).tolist()
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["c5_mix", "min_max", "more_than_cus"])
+def test_balanced_units_table_and_parity(kind):
+    """The automatic plan of the 128-head d_s = 256 kernel: its unit table
+    against the brute-force unit map, and every sequence against the oracle."""
+    lens = _balanced_lens(kind)
+    case = make_case(CONFIGS["ragged_tp2"], batch=len(lens), ctx=lens, seed=77)
+    print(f"balanced units: {kind}, batch {len(lens)}, max len {max(lens)}", flush=True)
+    o, l, table = balanced_shard_decode(case, g=1)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    _, want = unit_map_reference(case.seq_lens, cus, 1024, int(case.seq_lens.max()))
+    assert np.array_equal(table.astype(np.int64), want)
+    worst = 0.0
     for b in range(case.cfg.batch):
-        _, parts = oracle_step(case, b, 2, hadamard=False, with_new=False, q_is_rotated=True)
-        assert rel_err(host_f64(o)[b], parts[0][0]) <= TOL_BF16, b
+        _, parts = oracle_step(case, b, 2, hadamard=True)
+        err = rel_err(o[b].astype(np.float64), parts[1][0])
+        worst = max(worst, err)
+        assert err <= TOL_BF16, (b, int(case.seq_lens[b]))
+        assert np.max(np.abs(l[b] - parts[1][1])) <= 2e-2, b
+    print(f"  worst max|err|/max|ref| {worst:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("lens", [[1, 2, 63, 64], [65, 127, 128, 129], [4096, 1, 1000, 3]])
