@@ -236,7 +236,10 @@ typedef struct tpla_decode_args {
   int32_t num_splits;          /* token splits per sequence; 0 = automatic.     */
                                /* A request: raised where a kernel caps the     */
                                /* tokens of one split (65536 on the bf16        */
-                               /* streaming kernels)                            */
+                               /* streaming kernels).  Automatic on the 128-    */
+                               /* head d_s = 256 kernel: units of equal tiles   */
+                               /* cut from the lengths on the device (see       */
+                               /* tpla_decode_shard)                            */
 } tpla_decode_args;
 
 /*
@@ -256,7 +259,9 @@ tpla_status tpla_decode_workspace_size(const tpla_decode_args* args, size_t* byt
  * units in launch order, their XCD, one or two workgroups per CU, a fixed
  * start and finish per unit) and returns the count with the shortest
  * modelled launch, preferring fewer splits on ties.  For shapes that do not
- * run the streaming kernel it returns the automatic count.  It reads
+ * run the streaming kernel it returns the automatic count, and for the
+ * 128-head d_s = 256 kernel, whose automatic plan balances units over the
+ * device's lengths itself, it returns 0 (automatic).  It reads
  * nothing on the device and launches nothing; args->num_splits is ignored.
  * Errors: as tpla_decode_workspace_size; TPLA_ERR_NULL for a NULL
  * seq_lens_host or num_splits.
@@ -281,7 +286,12 @@ tpla_status tpla_decode_suggest_splits(const tpla_decode_args* args, const int32
  *
  * The work is split over tokens; each split keeps a running max and sum
  * (online softmax) and the splits are merged by log-sum-exp before `out` is
- * written.
+ * written.  On the 128-head d_s = 256 kernel the splits are work units
+ * derived on the device from seq_lens: with num_splits = 0, sequence b's
+ * ceil(L_b / 64) tiles are cut into units of c tiles, c the smallest chunk
+ * that leaves at most one unit per CU (capped at 1024 tiles), so a ragged
+ * batch gives every CU about the same work; with num_splits > 0 the chunk
+ * is the uniform one of that many splits of max_seq_len.
  *
  * Kernels: with dtype BF16, 16-byte aligned q_latent/q_rope/cache and query
  * strides that are multiples of 8,
