@@ -8,11 +8,12 @@ Sources (web pages about arXiv 2508.15881, "TPLA: Tensor Parallel Latent
 Attention for Efficient Disaggregated Prefill & Decode Inference"):
 
 * [ABS]  The English abstract, as shown on the chatpaper.ai, fugumt.com and
-  searcharxiv.org pages.  MLA caches one low-rank latent per token; TPLA
-  splits that latent and each head's input dimension across devices, runs
-  attention on every shard on its own, and sums the shard results with an
-  all-reduce; a Hadamard (or PCA) transform applied before the split reduces
-  the error between shards; every head still sees the whole latent.
+  searcharxiv.org pages.  In our words: the per-token cache is MLA's one
+  compressed latent; TPLA cuts it, and every head's input width with it,
+  into T slices held on T devices; each device runs the attention of all
+  heads over its own slice and the T results are added by an all-reduce;
+  an orthogonal transform (Hadamard, or PCA) is applied to the latent first
+  so the slices disagree less; no head loses access to any latent column.
 * [ABS-R] The revised English abstract on the paperbot-e5f.pages.dev page: it
   names the cached latent ``cKV``, calls the transforms orthogonal
   reparameterisations of RMSNorm and softmax, and keeps MLA for prefill and

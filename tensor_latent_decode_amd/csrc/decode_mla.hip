@@ -1,8 +1,9 @@
 // Streaming bf16 matrix-core split-K decode over a 512-wide latent with a
 // 64-wide rope (gfx950): the shape of plain MLA under tensor parallelism,
 // where every device keeps the whole latent for its share of the heads
-// (TPLA abstract: under TP each device must load the full cache; the
-// comparison TPLA is measured against).  It is also a TPLA "shard" at T = 1.
+// (TPLA abstract: plain MLA split by heads streams the entire latent cache
+// on each device, the baseline TPLA is compared with).  It is also a TPLA
+// "shard" at T = 1.
 //
 // One workgroup of four waves per (token split, sequence, group of 64, 32
 // or 16 heads).  Tiles of 32 tokens (one contiguous run of 32 * 576 * 2
