@@ -781,35 +781,63 @@ def test_dsv3_4k_full():
         assert rel_err(host_f64(outs[g])[0], parts[g][0]) <= TOL_BF16
 
 
+# Real-size configurations decode long sequences, where the bf16 rounding of
+# the softmax weights averages out: their worst error is watched against a
+# tighter bound than the general one, so that a change eating into the
+# margin shows before it crosses TOL_BF16.
+TOL_BF16_WATCH = 4.5e-3
+
+
 @pytest.mark.parametrize("name", ["dsv3_32k", "kimi_k2_32k", "mla_tp2_32k", "mla_tp4_32k"])
-def test_32k_shard_sampled(name):
-    """One shard (g = 0) at its real shape, automatic splits as the bench runs it."""
+def test_32k_every_shard_every_sequence(name):
+    """Every shard at its real shape with the split count the bench uses
+    (the host-side suggestion from the lengths), every sequence and head
+    against the oracle: output and lse."""
     case = make_case(CONFIGS[name])
     gc = GpuCase(case)
     cfg = case.cfg
-    d_s = cfg.d_s
+    B, H, d_s = cfg.batch, cfg.heads, cfg.d_s
+    maxlen = int(case.seq_lens.max())
     q = tpla.hadamard_latent(gc.q_latent)
     new = tpla.hadamard_latent(gc.new_latent)
-    cache = gc.prefill(0, d_s)
-    tpla.append_kv(cache, gc.bt, gc.new_seq, gc.new_pos, new[:, :d_s], gc.new_rope)
-    o, _ = tpla.decode_shard(q[:, :, :d_s], gc.q_rope, cache, gc.bt, gc.seq_lens, cfg.scale,
-                             int(case.seq_lens.max()))
-    torch.cuda.synchronize()
-    got = host_f64(o)
-    for b in (0, cfg.batch // 2, cfg.batch - 1):
-        _, parts = oracle_step(case, b, cfg.tp, hadamard=True)
-        assert rel_err(got[b], parts[0][0]) <= TOL_BF16, b
+    refs = [oracle_step(case, b, cfg.tp, hadamard=True)[1] for b in range(B)]
+    for g in range(cfg.tp):
+        cache = gc.prefill(g, d_s)
+        tpla.append_kv(cache, gc.bt, gc.new_seq, gc.new_pos, new[:, g * d_s:(g + 1) * d_s],
+                       gc.new_rope)
+        qs = q[:, :, g * d_s:(g + 1) * d_s]
+        out = torch.full((B, H, d_s), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
+        args = tpla.make_decode_args(qs, gc.q_rope, cache, gc.bt, gc.seq_lens, cfg.scale, maxlen,
+                                     out, lse, 0)
+        splits = tpla.decode_suggest_splits(args, case.seq_lens)
+        tpla.decode_shard(qs, gc.q_rope, cache, gc.bt, gc.seq_lens, cfg.scale, maxlen, out=out,
+                          lse=lse, num_splits=splits)
+        torch.cuda.synchronize()
+        got, got_lse = host_f64(out), host_f64(lse)
+        del cache
+        worst = max(rel_err(got[b], refs[b][g][0]) for b in range(B))
+        worst_lse = max(float(np.max(np.abs(got_lse[b] - refs[b][g][1]))) for b in range(B))
+        print(f"{name} shard {g} splits {splits}: worst max|err|/max|ref| {worst:.3e}, "
+              f"worst |lse err| {worst_lse:.3e}", flush=True)
+        assert worst <= TOL_BF16_WATCH, (name, g, worst)
+        assert worst_lse <= 2e-2, (name, g, worst_lse)
 
 
-def test_ragged_tp2_full_step_sampled():
+def test_ragged_tp2_full_step_every_sequence():
+    """The ragged TP = 2 step as the bench runs it (both shards, automatic
+    plan, combined output), every sequence against the oracle."""
     case = make_case(CONFIGS["ragged_tp2"])
     gc = GpuCase(case)
     combined, _, _ = run_step(gc, hadamard=True)
     got = host_f64(combined)
-    order = np.argsort(case.seq_lens)
-    for b in (int(order[0]), int(order[-1]), 7):
+    worst = 0.0
+    for b in range(case.cfg.batch):
         ref, _ = oracle_step(case, b, 2, hadamard=True)
-        assert rel_err(got[b], ref) <= TOL_BF16, (b, int(case.seq_lens[b]))
+        err = rel_err(got[b], ref)
+        worst = max(worst, err)
+        assert err <= TOL_BF16_WATCH, (b, int(case.seq_lens[b]), err)
+    print(f"ragged_tp2: worst max|err|/max|ref| {worst:.3e}", flush=True)
 
 
 # --------------------------------------------------------------------------
