@@ -94,25 +94,28 @@ def kernel_source_hash() -> str:
     csrc = os.path.join(ROOT, "tensor_latent_decode_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.startswith("decode_") or name in ("tpla_api.hip", "merge_combine.hip",
-                                                  "tpla_internal.h"):
+                                                  "tpla_internal.h", "unit_map.h"):
             h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per decode launch from committed rocprofv3 counters, if they
-    were taken on the current kernel sources (else None)."""
+def stored_counters(workload: str):
+    """Figures per decode launch from committed rocprofv3 counter runs
+    (profiles/decode_<workload>_traffic.json), if they were taken on the
+    current kernel sources: (record, None), else (None, reason)."""
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
     if not os.path.exists(path):
-        return None
+        return None, f"no counter record for {workload}"
     rec = json.load(open(path))
     if rec.get("kernel_sha") != kernel_source_hash():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return None, (f"counters were taken on kernel sources {rec.get('kernel_sha')}, these are "
+                      f"{kernel_source_hash()}")
+    return rec, None
 
 
-def run_copy(torch, steps):
-    n = 1 << 30
+def copy_probe(torch, steps, n=1 << 30):
+    """A plain device copy of n bytes (read n, write n), timed with events:
+    the HBM rate a streaming kernel can reach on this GPU, in GB/s."""
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     src.fill_(1)
@@ -127,19 +130,49 @@ def run_copy(torch, steps):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
-    print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
-                      "ms_per_copy": ms, "copy_GBps": 2 * n / ms / 1e6}), flush=True)
+    del src, dst
+    return {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "ms_per_copy": ms,
+            "copy_GBps": 2 * n / ms / 1e6}
+
+
+def run_copy(torch, steps):
+    print(json.dumps({"mode": "copy", **copy_probe(torch, steps)}), flush=True)
+
+
+def host_cpu():
+    """(CPU model, cores this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def timed_reps(fn, reps=3):
+    """One untimed warm-up run, then the median of `reps` timed runs (s)."""
+    fn()
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[len(ts) // 2]
 
 
 def cpu_baseline(case, seconds: float):
-    """The fp64 oracle over whole sequences of the same workload, on the host."""
+    """The fp64 oracle over whole sequences of the same workload, on the host:
+    one warm-up and three timed runs over a sample of sequences (median), with
+    the BLAS thread pool as it is and again limited to one thread."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:           # pragma: no cover - threadpoolctl is optional
-        threads = len(os.sched_getaffinity(0))
+    from threadpoolctl import threadpool_info, threadpool_limits
+    model, cores = host_cpu()
+    blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     cfg = case.cfg
     d_s, tp = cfg.d_s, cfg.tp
     shards = list(range(tp)) if cfg.name == "ragged_tp2" else [0]
@@ -147,21 +180,23 @@ def cpu_baseline(case, seconds: float):
     bs = cfg.block_size
     f64 = oracle.bf16_bits_to_f64
     starts = np.concatenate([[0], np.cumsum(case.seq_lens - 1)])
-    done_bytes = 0
-    done_seqs = 0
-    elapsed = 0.0
-    for b in range(cfg.batch):
+
+    def caches_of(b):
+        """Sequence b's paged cache per shard with its history rows (set-up)."""
         n = int(case.seq_lens[b]) - 1
         rows = slice(int(starts[b]), int(starts[b]) + n)
-        # this sequence's paged cache per shard (history rows: set-up, not timed)
-        caches = []
+        out = []
         for g in shards:
             cache = np.zeros((case.num_blocks, bs, d_s + cfg.d_r), np.uint16)
             oracle.paged_append(cache, case.block_table, bs, case.hist_seq[rows],
                                 case.hist_pos[rows], case.hist_latent[rows, g * d_s:(g + 1) * d_s],
                                 case.hist_rope[rows])
-            caches.append(cache)
-        t0 = time.perf_counter()
+            out.append(cache)
+        return out
+
+    def step_seq(b, caches):
+        """The step for sequence b: rotate, append the new row, attention per
+        shard, combine (the appended row is rewritten identically each run)."""
         q = f64(case.q_latent[b])
         new = f64(case.new_latent[b])[None]
         if rotate:
@@ -177,17 +212,41 @@ def cpu_baseline(case, seconds: float):
                 case.block_table[b:b + 1], case.seq_lens[b:b + 1], bs, d_s, cfg.scale)
             outs.append(o)
         oracle.combine_shards(outs)
-        elapsed += time.perf_counter() - t0
-        done_bytes += int(case.seq_lens[b]) * (d_s + cfg.d_r) * 2 * len(shards)
-        done_seqs += 1
-        if elapsed >= seconds:
-            break
-    return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": int(threads),
+
+    def seq_bytes(seqs):
+        return sum(int(case.seq_lens[b]) for b in seqs) * (d_s + cfg.d_r) * 2 * len(shards)
+
+    # sample: as many sequences as fit a quarter of the budget per (warm-up +
+    # 3 runs) of the pool as it is; the one-thread runs take a quarter more
+    order = list(range(cfg.batch))
+    caches = {0: caches_of(0)}
+    t0 = time.perf_counter()
+    step_seq(0, caches[0])
+    per_seq = max(time.perf_counter() - t0, 1e-6)
+    n_multi = int(max(1, min(cfg.batch, seconds / 4 / 4 / per_seq)))
+    seqs = order[:n_multi]
+    for b in seqs:
+        if b not in caches:
+            caches[b] = caches_of(b)
+    med = timed_reps(lambda: [step_seq(b, caches[b]) for b in seqs])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        step_seq(0, caches[0])
+        per_seq1 = max(time.perf_counter() - t0, 1e-6)
+        n_one = int(max(1, min(n_multi, seconds / 4 / 4 / per_seq1)))
+        seqs1 = order[:n_one]
+        med1 = timed_reps(lambda: [step_seq(b, caches[b]) for b in seqs1])
+    what = (f"whole step per sequence: {'rotate, ' if rotate else ''}append, paged gather + fp64 "
+            f"attention per shard, combine")
+    return {"value": seq_bytes(seqs) / med / 1e9, "unit": "GB/s", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": f"{done_seqs} of {cfg.batch} sequences of the same workload (whole step "
-                      f"per sequence: {'rotate, ' if rotate else ''}append, paged gather + fp64 "
-                      f"attention per shard, combine), {elapsed:.1f} s on the host; tokens/s "
-                      f"{done_seqs / elapsed:.3g}"}
+            "sample": f"{len(seqs)} of {cfg.batch} sequences of the same workload ({what}); "
+                      f"median of 3 runs after 1 warm-up, {med:.2f} s each; tokens/s "
+                      f"{len(seqs) / med:.3g}",
+            "cpu_model": model, "host_cores": cores, "blas_threads": int(blas_threads),
+            "single_thread": {"value": seq_bytes(seqs1) / med1 / 1e9, "unit": "GB/s", "cores": 1,
+                              "sample": f"{len(seqs1)} sequences, median of 3 runs after 1 "
+                                        f"warm-up, {med1:.2f} s each"}}
 
 
 PREFILL_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix cores, vendor figure
@@ -209,6 +268,7 @@ def cpu_prefill_baseline(pc, seconds: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:           # pragma: no cover - threadpoolctl is optional
         threads = len(os.sched_getaffinity(0))
+    model, cores = host_cpu()
     f64 = oracle.bf16_bits_to_f64
     d_c = pc.cfg.d_c
     n, done, elapsed, dt = 64, 0, 0.0, 0.0
@@ -227,7 +287,8 @@ def cpu_prefill_baseline(pc, seconds: float):
     return {"value": done / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"prefixes of 64..{last} tokens of the first prompt (all {pc.cfg.heads} heads), "
-                      f"{elapsed:.1f} s on the host"}
+                      f"{elapsed:.1f} s on the host",
+            "cpu_model": model, "host_cores": cores}
 
 
 def run_prefill(args, torch):
@@ -487,14 +548,22 @@ def main():
 
     torch.cuda.synchronize()
     full, rest = divmod(args.steps, per_cycle)
+    # one event between consecutive replays: per-window step times
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(full + 1)]
     ev0.record()
-    for _ in range(full):
+    marks[0].record()
+    for k in range(full):
         cycle.replay()
+        marks[k + 1].record()
     for k in range(rest):
         graphs[k % replicas].replay()
     ev1.record()
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
+    windows = sorted(marks[k].elapsed_time(marks[k + 1]) / per_cycle for k in range(full))
+
+    def pct(q):
+        return windows[min(len(windows) - 1, int(q * len(windows)))] if windows else ms_step
 
     # decode kernel alone: back-to-back launches on the same stream
     d0 = torch.cuda.Event(enable_timing=True)
@@ -510,12 +579,16 @@ def main():
     torch.cuda.synchronize()
     ms_dec = d0.elapsed_time(d1) / (reps * n_dec)
 
+    del graphs, cycle, dec_graph
+    probe = copy_probe(torch, 10)
+
     lens_sum = int(np.sum(case.seq_lens.astype(np.int64)))
     bytes_per_shard = lens_sum * (d_s + d_r) * 2
     step_bytes = bytes_per_shard * len(shards)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = bytes_per_shard / (ms_dec * 1e-3) / 1e9
-    traffic = stored_traffic(args.workload)
+    counters, why_not = stored_counters(args.workload)
+    traffic = counters.get("hbm_bytes_per_launch") if counters else None
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -525,6 +598,9 @@ def main():
         "warmup": args.warmup,
         "warmup_steps_run": warm_steps,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_windows": {"windows": len(windows), "steps_per_window": per_cycle,
+                                "median": round(pct(0.5), 5), "p10": round(pct(0.1), 5),
+                                "p90": round(pct(0.9), 5)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -538,10 +614,15 @@ def main():
                    "latent_norm": args.latent_norm, "up_project_d_v": args.up_project,
                    "seq_len": maxlen},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "copy_probe_GBps": round(probe["copy_GBps"], 1),
+        "pct_of_copy_probe": round(100.0 * value / probe["copy_GBps"], 2),
         "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
+                     "traffic_source": (counters.get("source") if counters else why_not),
+                     "mfma_busy_pct": counters.get("mfma_busy_pct") if counters else None,
+                     "pct_of_copy_probe": round(100.0 * achieved / probe["copy_GBps"], 2),
                      "kernel": "tpla_decode_shard (split-K attention + LSE merge)",
                      "ms_per_launch": round(ms_dec, 5),
                      "algorithmic_bytes_per_launch": bytes_per_shard},
