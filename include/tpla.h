@@ -48,7 +48,17 @@
 extern "C" {
 #endif
 
-typedef enum tpla_status {
+/* The enums of this interface are 32-bit integers.  A caller may pass any
+ * value (the library checks it): C++ sees them with int32_t as the fixed
+ * underlying type, which makes every int32_t value a valid one, and C
+ * compilers lay them out as int. */
+#ifdef __cplusplus
+#define TPLA_ENUM(name) enum name : int32_t
+#else
+#define TPLA_ENUM(name) enum name
+#endif
+
+typedef TPLA_ENUM(tpla_status) {
   TPLA_OK = 0,
   TPLA_ERR_NULL = 1,        /* a required pointer is NULL                      */
   TPLA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent          */
@@ -59,7 +69,7 @@ typedef enum tpla_status {
   TPLA_ERR_HIP = 7          /* the HIP runtime reported an error               */
 } tpla_status;
 
-typedef enum tpla_dtype {
+typedef TPLA_ENUM(tpla_dtype) {
   TPLA_FP32 = 0,
   TPLA_BF16 = 1
 } tpla_dtype;
@@ -270,6 +280,16 @@ tpla_status tpla_decode_suggest_splits(const tpla_decode_args* args, const int32
                                        int32_t* num_splits);
 
 /*
+ * tpla_decode_suggest_splits_cus: the same suggestion for a device with
+ * `cus` compute units, without querying any device (a scheduler planning
+ * for a GPU it does not drive; tests on a host without one).
+ * Errors: as tpla_decode_suggest_splits; TPLA_ERR_SHAPE for cus < 1.
+ */
+tpla_status tpla_decode_suggest_splits_cus(const tpla_decode_args* args,
+                                           const int32_t* seq_lens_host, int32_t cus,
+                                           int32_t* num_splits);
+
+/*
  * tpla_decode_shard: one device's share of a TPLA decode step.
  *
  * Per-shard attention with the shard's own softmax (abstract: attention is
@@ -450,8 +470,9 @@ typedef struct tpla_prefill_args {
  */
 tpla_status tpla_mla_prefill(const tpla_prefill_args* args, void* stream);
 
-/* Static text for a status code. */
-const char* tpla_status_string(tpla_status status);
+/* Static text for a status code: a tpla_status value, passed as an
+ * integer so that any value is valid ("unknown status" outside the enum). */
+const char* tpla_status_string(int32_t status);
 /* Message of the last failed call on this thread ("" if none). */
 const char* tpla_last_error(void);
 /* Library version as major*10000 + minor*100 + patch. */

@@ -138,13 +138,16 @@ struct Plan {
 
 size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
-tpla_status plan_decode(const tpla_decode_args* a, Plan* pl) {
+// cus_given > 0: plan for a device with that many CUs (no device query).
+tpla_status plan_decode(const tpla_decode_args* a, Plan* pl, int cus_given = 0) {
   const int maxlen = a->max_seq_len;
   int want = a->num_splits;
-  int cus = 0;
-  if (want == 0) {
+  int cus = cus_given;
+  if (want == 0 && cus <= 0) {
     const tpla_status st = device_cus(&cus);
     if (st != TPLA_OK) return st;
+  }
+  if (want == 0) {
     int64_t groups = a->batch;
     int per_cu = 2;
     const Path path = decode_path(a);
@@ -225,20 +228,22 @@ double stream_launch_cost(const int32_t* lens, int batch, int hg, int max_len, i
   return worst;
 }
 
-}  // namespace
-
-extern "C" {
-
-tpla_status tpla_decode_suggest_splits(const tpla_decode_args* args, const int32_t* seq_lens_host,
-                                       int32_t* num_splits) {
+// The split suggestion for a device of `cus` CUs (<= 0: query the current
+// device).
+tpla_status suggest_splits(const tpla_decode_args* args, const int32_t* seq_lens_host, int cus,
+                           int32_t* num_splits) {
   if (num_splits == nullptr || seq_lens_host == nullptr)
     return fail(TPLA_ERR_NULL, "seq_lens_host and num_splits are required");
   tpla_status st = check_decode(args);
   if (st != TPLA_OK) return st;
+  if (cus <= 0) {
+    st = device_cus(&cus);
+    if (st != TPLA_OK) return st;
+  }
   tpla_decode_args a = *args;
   a.num_splits = 0;
   Plan pl;
-  st = plan_decode(&a, &pl);
+  st = plan_decode(&a, &pl, cus);
   if (st != TPLA_OK) return st;
   if (decode_path(&a) != Path::kStream) {
     *num_splits = pl.splits;
@@ -249,9 +254,6 @@ tpla_status tpla_decode_suggest_splits(const tpla_decode_args* args, const int32
     *num_splits = 0;
     return ok();
   }
-  int cus = 0;
-  st = device_cus(&cus);
-  if (st != TPLA_OK) return st;
   const int hg = a.heads / tpla::decode_latsplit_heads_per_group(a.heads, a.d_s);
   const int per_cu = tpla::decode_latsplit_groups_per_cu(a.heads, a.d_s);
   const int max_tiles = std::max(1, (a.max_seq_len + 63) / 64);
@@ -272,7 +274,23 @@ tpla_status tpla_decode_suggest_splits(const tpla_decode_args* args, const int32
   return ok();
 }
 
-const char* tpla_status_string(tpla_status s) {
+}  // namespace
+
+extern "C" {
+
+tpla_status tpla_decode_suggest_splits(const tpla_decode_args* args, const int32_t* seq_lens_host,
+                                       int32_t* num_splits) {
+  return suggest_splits(args, seq_lens_host, 0, num_splits);
+}
+
+tpla_status tpla_decode_suggest_splits_cus(const tpla_decode_args* args,
+                                           const int32_t* seq_lens_host, int32_t cus,
+                                           int32_t* num_splits) {
+  if (cus < 1) return fail(TPLA_ERR_SHAPE, "cus must be >= 1 (got %d)", cus);
+  return suggest_splits(args, seq_lens_host, cus, num_splits);
+}
+
+const char* tpla_status_string(int32_t s) {
   switch (s) {
     case TPLA_OK: return "ok";
     case TPLA_ERR_NULL: return "null pointer";

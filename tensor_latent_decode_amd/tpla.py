@@ -17,7 +17,9 @@ from typing import List, Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtpla.so")
+# TPLA_LIB names another build of the same library (the host-side
+# sanitizer build, tensor_latent_decode_amd/build_sanitize.py)
+LIB_PATH = os.environ.get("TPLA_LIB") or os.path.join(_HERE, "libtpla.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tpla.h")
 
 FP32, BF16 = 0, 1
@@ -117,12 +119,15 @@ def lib() -> ctypes.CDLL:
     L.tpla_combine_shards.argtypes = [ctypes.POINTER(vp), dt, i32, i32, i32, i32, vp, dt, i32, vp]
     L.tpla_rotate_append.argtypes = [ctypes.POINTER(RotateAppendArgs), vp]
     L.tpla_decode_suggest_splits.argtypes = [ctypes.POINTER(DecodeArgs), vp, ctypes.POINTER(i32)]
+    L.tpla_decode_suggest_splits_cus.argtypes = [ctypes.POINTER(DecodeArgs), vp, i32,
+                                                 ctypes.POINTER(i32)]
     L.tpla_up_project.argtypes = [vp, dt, i64, i64, vp, dt, i64, i64, vp, dt, i64, i64,
                                   i32, i32, i32, i32, i32, vp]
     L.tpla_mla_prefill.argtypes = [ctypes.POINTER(PrefillArgs), vp]
     for f in ("tpla_hadamard_latent", "tpla_append_kv", "tpla_decode_workspace_size",
               "tpla_decode_shard", "tpla_decode_shard_noalloc", "tpla_combine_shards", "tpla_rotate_append",
-              "tpla_decode_suggest_splits", "tpla_up_project", "tpla_mla_prefill"):
+              "tpla_decode_suggest_splits", "tpla_decode_suggest_splits_cus", "tpla_up_project",
+              "tpla_mla_prefill"):
         getattr(L, f).restype = ctypes.c_int
     L.tpla_status_string.argtypes = [ctypes.c_int]
     L.tpla_status_string.restype = ctypes.c_char_p
@@ -388,16 +393,22 @@ def make_decode_args(q_latent: torch.Tensor, q_rope: Optional[torch.Tensor], cac
     return a
 
 
-def decode_suggest_splits(args: "DecodeArgs", seq_lens_host) -> int:
-    """Split count for `args` from the host copy of the sequence lengths."""
+def decode_suggest_splits(args: "DecodeArgs", seq_lens_host, cus: Optional[int] = None) -> int:
+    """Split count for `args` from the host copy of the sequence lengths, for
+    the current device, or for a device of `cus` CUs (no device query)."""
     import numpy as np
     lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
     if lens.shape != (args.batch,):
         raise ValueError("seq_lens_host must hold one length per sequence")
     out = ctypes.c_int32(0)
-    _check("tpla_decode_suggest_splits",
-           lib().tpla_decode_suggest_splits(ctypes.byref(args), lens.ctypes.data_as(ctypes.c_void_p),
-                                            ctypes.byref(out)))
+    ptr = lens.ctypes.data_as(ctypes.c_void_p)
+    if cus is None:
+        _check("tpla_decode_suggest_splits",
+               lib().tpla_decode_suggest_splits(ctypes.byref(args), ptr, ctypes.byref(out)))
+    else:
+        _check("tpla_decode_suggest_splits_cus",
+               lib().tpla_decode_suggest_splits_cus(ctypes.byref(args), ptr, int(cus),
+                                                    ctypes.byref(out)))
     return int(out.value)
 
 

@@ -4,6 +4,7 @@ rejects bad host arguments before touching the GPU (no compute calls)."""
 import ctypes
 import os
 
+import numpy as np
 import pytest
 
 from tensor_latent_decode_amd import tpla
@@ -226,6 +227,55 @@ def test_suggest_splits_argument_checks():
     a.d_s = 0
     _fails(L.tpla_decode_suggest_splits(ctypes.byref(a), ctypes.cast(lens, ctypes.c_void_p),
                                         ctypes.byref(out)), 2)
+
+
+def test_suggest_splits_for_a_given_cu_count():
+    """The cost model without a device: uniform 32K lengths keep the automatic
+    count on the 64-head streaming kernel (16 sequences x 64 heads over 256
+    CUs at two workgroups per CU: 32 splits), the 128-head kernel defers to its
+    own balanced plan (0), and a bad CU count is refused."""
+    L = tpla.lib()
+    lens = np.full(16, 32768, np.int32)
+    kimi = _args(batch=16, heads=64, d_s=128, num_blocks=8193, max_blocks_per_seq=512,
+                 max_seq_len=32768, q_latent_stride_b=64 * 512, q_rope_stride_b=64 * 64,
+                 out_stride_b=64 * 128, out_stride_h=128)
+    assert tpla.decode_suggest_splits(kimi, lens, cus=256) == 32
+    dsv3 = _args(batch=16, num_blocks=8193, max_blocks_per_seq=512, max_seq_len=32768)
+    assert tpla.decode_suggest_splits(dsv3, lens, cus=256) == 0
+    out = ctypes.c_int32(0)
+    _fails(L.tpla_decode_suggest_splits_cus(ctypes.byref(dsv3), lens.ctypes.data_as(ctypes.c_void_p),
+                                            0, ctypes.byref(out)), 2)
+
+
+def test_suggest_splits_fuzz():
+    """Random shapes, lengths (zeros, negatives and lengths past max_seq_len
+    included) and CU counts: the suggestion is always a valid split count."""
+    rng = np.random.default_rng(2024)
+    for _ in range(300):
+        B = int(rng.integers(1, 65))
+        heads, d_s = [(128, 256), (64, 128), (256, 256), (16, 512), (5, 80), (32, 64)][rng.integers(6)]
+        d_r = int([0, 64, 8][rng.integers(3)])
+        bs = int([16, 32, 64, 128][rng.integers(4)])
+        maxlen = int(rng.integers(0, 70001))
+        mb = max(1, -(-maxlen // bs)) + int(rng.integers(0, 3))
+        a = _args(batch=B, heads=heads, d_s=d_s, d_r=d_r, block_size=bs, num_blocks=B * mb + 1,
+                  max_blocks_per_seq=mb, max_seq_len=maxlen,
+                  q_latent_stride_b=heads * 512, q_latent_stride_h=512,
+                  q_rope_stride_b=heads * 64, q_rope_stride_h=64,
+                  out_stride_b=heads * d_s, out_stride_h=d_s, num_splits=int(rng.integers(0, 5)))
+        lens = rng.integers(-5, maxlen + 100, size=B).astype(np.int32)
+        cus = int(rng.integers(1, 513))
+        try:
+            got = tpla.decode_suggest_splits(a, lens, cus=cus)
+        except tpla.TplaError as e:       # a shape no kernel serves
+            assert e.status == 5, (heads, d_s, d_r, e)
+            continue
+        assert 0 <= got <= max(1, -(-maxlen // 64)), (B, heads, d_s, maxlen, got)
+        a.num_splits = got
+        n = ctypes.c_size_t()
+        # the suggestion plans without a device query unless it is 0 (automatic)
+        if got > 0:
+            assert tpla.lib().tpla_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
 
 
 def test_up_project_argument_checks():
