@@ -37,6 +37,30 @@
  *  - bf16 means IEEE binary32 truncated to its top 16 bits (uint16 storage);
  *    every float32 -> bf16 conversion rounds to nearest, ties to even.
  *  - No function throws; all are thread-safe (the error text is per thread).
+ *
+ * Choices a caller of the bare method (rotate, append, decode, combine)
+ * should know about:
+ *  - Argument order: every buffer is followed by its own dtype and row
+ *    stride, e.g. tpla_hadamard_latent(x, x_dtype, x_row_stride, y,
+ *    y_dtype, y_row_stride, rows, n, stream); n may be up to 4096.
+ *    tpla_append_kv also takes `batch`, the rows of the block table, so a
+ *    row naming another sequence is skipped instead of reading past the
+ *    table.
+ *  - Alignment: the bf16 matrix-core decode kernels need 16-byte aligned
+ *    operands; a shape they serve fails with TPLA_ERR_ALIGN when the
+ *    operands miss it, rather than running the float32 kernel some 400x
+ *    slower.  Shapes no matrix-core kernel serves run the float32 kernel at
+ *    any alignment.
+ *  - Device data: there is no separate checking build.  Every kernel clamps
+ *    what it reads from device memory (an out-of-range block id reads the
+ *    cache's first rows, a length past max_seq_len is cut to it, a row past
+ *    its sequence's blocks is skipped), at no cost to the fast path: bad
+ *    data gives unspecified output and no access outside the buffers.
+ *  - Enumerations are 32-bit integers; any value may be passed (checked).
+ *  - Beyond the four calls: tpla_rotate_append (rotation and append in one
+ *    launch), tpla_decode_suggest_splits(_cus) (split count from host-side
+ *    lengths), tpla_decode_shard_noalloc (no workspace), tpla_up_project,
+ *    tpla_mla_prefill.
  */
 #ifndef TPLA_H_
 #define TPLA_H_
@@ -324,7 +348,10 @@ tpla_status tpla_decode_suggest_splits_cus(const tpla_decode_args* args,
  *     its heads; TPLA abstract), or one shard at T = 1;
  *   - a register-staged matrix-core kernel serves heads % 32 == 0 with d_s
  *     in {64, 128, 256} and d_r in {0, 64};
- * every other case (and FP32) runs a float32 kernel, which needs
+ * a bf16 shape that one of these serves but whose operands miss the
+ * alignment above fails with TPLA_ERR_ALIGN (the float32 kernel would take
+ * it some 400x slower); every other case (and FP32) runs a float32 kernel,
+ * which needs
  * 4*(24*(d_s + d_r) + 8*d_s + 152) <= 65536 bytes of LDS (e.g. d_s = 256,
  * d_r = 64 fits; d_s = 512, d_r = 64 does not: TPLA_ERR_UNSUPPORTED there).
  * out_dtype FP32 or BF16.
@@ -332,8 +359,9 @@ tpla_status tpla_decode_suggest_splits_cus(const tpla_decode_args* args,
  * aligned; its contents on entry do not matter.  The split outputs go there
  * (fp16 with a float scale per 64 columns on the streaming kernels, float32
  * otherwise) and a second kernel on the same stream merges them into `out`.
- * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE, TPLA_ERR_DTYPE, TPLA_ERR_UNSUPPORTED
- * (no kernel for the shape, above), TPLA_ERR_WORKSPACE, TPLA_ERR_HIP.
+ * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE, TPLA_ERR_ALIGN (bf16 operands or
+ * workspace misaligned, above), TPLA_ERR_DTYPE, TPLA_ERR_UNSUPPORTED (no
+ * kernel for the shape, above), TPLA_ERR_WORKSPACE, TPLA_ERR_HIP.
  */
 tpla_status tpla_decode_shard(const tpla_decode_args* args, void* workspace,
                               size_t workspace_bytes, void* stream);

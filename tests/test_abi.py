@@ -171,6 +171,25 @@ def test_decode_argument_checks(kw, code):
     _fails(L.tpla_decode_shard(ctypes.byref(_args(**kw)), FAKE, 1 << 40, None), code)
 
 
+def test_decode_misaligned_bf16_operands_are_refused():
+    # bf16 shapes with a matrix-core kernel need its alignment (the float32
+    # kernel would be two orders of magnitude slower); a shape no
+    # matrix-core kernel serves runs the float32 kernel at any alignment
+    L = tpla.lib()
+    n = ctypes.c_size_t()
+    for kw in (dict(q_latent=FAKE + 2), dict(cache=FAKE + 8), dict(q_rope=FAKE + 4),
+               dict(q_latent_stride_h=516), dict(q_rope_stride_b=128 * 64 + 4)):
+        _fails(L.tpla_decode_workspace_size(ctypes.byref(_args(**kw)), ctypes.byref(n)), 3)
+        _fails(L.tpla_decode_shard(ctypes.byref(_args(**kw)), FAKE, 1 << 40, None), 3)
+    odd = _args(heads=5, d_s=80, d_r=8, q_latent=FAKE + 2, q_latent_stride_b=5 * 80,
+                q_latent_stride_h=80, q_rope_stride_b=5 * 8, q_rope_stride_h=8,
+                out_stride_b=5 * 80, out_stride_h=80)
+    assert L.tpla_decode_workspace_size(ctypes.byref(odd), ctypes.byref(n)) == 0
+    # float32 inputs have no alignment requirement
+    assert L.tpla_decode_workspace_size(ctypes.byref(_args(dtype=0, q_latent=FAKE + 4)),
+                                        ctypes.byref(n)) == 0
+
+
 def test_decode_null_args_and_workspace_checks():
     L = tpla.lib()
     n = ctypes.c_size_t()
