@@ -253,26 +253,18 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   // ---- split outputs ----
   // fp16 with one float scale per (row, 64-column block): o = scale * h,
   // |h| <= 1, which halves the traffic of the split merge at a rounding
-  // error below 2^-11 of the block's largest value.  The value waves put
-  // their columns into LDS (the K buffers, idle by then); then the whole
-  // workgroup writes the group's rows, which are one contiguous block of the
-  // workspace, with coalesced stores.
-  // Staged rows are DS + 8 halves apart: a value wave writes one row per
-  // lane pair, and rows a power-of-two apart would share their LDS banks.
-  constexpr int kStageRow = DS + 8;
-  uint16_t* stage_h = reinterpret_cast<uint16_t*>(&ktile[0][0]);              // [HG][kStageRow] fp16
-  float* stage_sc = reinterpret_cast<float*>(stage_h + HG * kStageRow);         // [HG][DS / 64]
-  auto store_split_outputs = [&]() {
-    barrier();                                      // the staged rows are complete
-    const int64_t row0g = row0 + head0;
-    uint64_t* dst = reinterpret_cast<uint64_t*>(reinterpret_cast<uint16_t*>(p.ws_o) + row0g * DS);
-    for (int i = static_cast<int>(threadIdx.x); i < HG * DS / 4; i += 512)
-      dst[i] = *reinterpret_cast<const uint64_t*>(stage_h + (i / (DS / 4)) * kStageRow + (i % (DS / 4)) * 4);
-    float* wsc = reinterpret_cast<float*>(reinterpret_cast<char*>(p.ws_o) +
-                                          fp16_partials_scale_offset(p.max_units, 1, p.heads, DS));
-    for (int i = static_cast<int>(threadIdx.x); i < HG * (DS / 64); i += 512)
-      wsc[row0g * (DS / 64) + i] = stage_sc[i];
-  };
+  // error below 2^-11 of the block's largest value.  The unit's rows are
+  // laid out as the value waves hold them: [column / 8][head][8 columns],
+  // so every store of a value wave writes 512 contiguous bytes straight
+  // from its accumulators; scales are [column / 64][head].
+  uint16_t* const part_h = reinterpret_cast<uint16_t*>(p.ws_o) + row0 * DS;
+  float* const part_sc = reinterpret_cast<float*>(reinterpret_cast<char*>(p.ws_o) +
+                                                  fp16_partials_scale_offset(p.max_units, 1, p.heads, DS)) +
+                         row0 * (DS / 64);
+  // With the merge inside the launch: once every wave's writes of this
+  // unit have reached the L2 (each wave waits for its own stores), one
+  // release by one thread (an L2 write-back) publishes them all and counts
+  // the unit in for its sequence.
 
   if (is_score) {
     // =====================================================================
@@ -491,7 +483,6 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
       p.ws_lse[row0 + head] = (m_run + __log2f(l_tot)) * kLn2;
     }
     barrier();                                    // B_l
-    store_split_outputs();
     return;
   }
 
@@ -639,21 +630,20 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     if (!any) break;
     barrier();                                    // B_r
   }
-  barrier();                                      // B_l: row sums in lsum
-
-  // this wave's columns of the split outputs, into LDS
+  // this wave's columns of the split outputs, from the accumulators: fp16
+  // of o / (block max), then after B_l the block's scale max / l
+  float amax_ht[NS];
 #pragma unroll
   for (int ht = 0; ht < NS; ++ht) {
-    const float inv_l = 1.0f / lsum[ht * 32 + l31];
     float amax = 0.f;
 #pragma unroll
     for (int mm = 0; mm < MPW; ++mm)
 #pragma unroll
       for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(oacc[mm][ht][r]));
     amax = both_halves_max(amax);
+    amax_ht[ht] = amax;
     const float hs = amax > 0.f ? 1.0f / amax : 0.f;
-    const int hrow = ht * 32 + l31;
-    uint16_t* dst = stage_h + hrow * kStageRow + 64 * lq + 4 * half;
+    const int head = head0 + ht * 32 + l31;
 #pragma unroll
     for (int mm = 0; mm < MPW; ++mm)
 #pragma unroll
@@ -666,11 +656,17 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
           w[k] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
         }
-        *reinterpret_cast<uint2*>(dst + mm * 32 + 8 * q) = make_uint2(w[0], w[1]);
+        const int cb = 8 * lq + 4 * mm + q;     // 8-column block of columns 64lq + 32mm + 8q ..
+        *reinterpret_cast<uint2*>(part_h + (static_cast<int64_t>(cb) * p.heads + head) * 8 + 4 * half) =
+            make_uint2(w[0], w[1]);
       }
-    if (half == 0) stage_sc[hrow * (DS / 64) + lq] = amax * inv_l;
   }
-  store_split_outputs();
+  barrier();                                      // B_l: row sums in lsum
+  if (half == 0) {
+#pragma unroll
+    for (int ht = 0; ht < NS; ++ht)
+      part_sc[lq * p.heads + head0 + ht * 32 + l31] = amax_ht[ht] / lsum[ht * 32 + l31];
+  }
 }
 
 // Tuning of the launch below (kept as named constants so the choice is

@@ -12,6 +12,7 @@
 // zero-padded shard outputs (the all-reduce of the TPLA abstract) places
 // them side by side.
 #include "tpla_internal.h"
+#include "merge_item.h"
 
 namespace tpla {
 namespace {
@@ -125,103 +126,37 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_ite
 }
 
 // fp16 split outputs (streaming kernels; d_s a multiple of blk_cols, which
-// is a multiple of 8): one thread per (b, h, 8 consecutive columns), so a
-// wavefront reads two whole 256-column rows of a split with 16-byte loads.
-// Up to 16 splits per memory round trip, as above.  The splits of sequence
-// b are either rows (s, b, h) for s < splits, or (unit table) rows
-// (first_b + s, h) for s < n_b.
-template <bool kBf16Out>
+// is a multiple of 8): one thread per (b, h, 8 consecutive columns) with
+// 16-byte partial loads, up to 16 splits per memory round trip, as above.
+// Two layouts:
+//   rows (s, b, h) for s < splits, each [d_s] with scales [d_s / blk_cols]:
+//     threads take the columns of a row fastest (a wavefront reads two whole
+//     256-column rows of a split);
+//   kUnits: sequence b owns units first_b .. first_b + n_b - 1 (unit
+//     table); unit u holds [d_s / 8][heads][8] halves and scales
+//     [d_s / blk_cols][heads]: threads take the heads fastest, so a
+//     wavefront reads 1 KB of one unit at a time.
+template <bool kBf16Out, bool kUnits>
 __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_items, int per_xcd) {
   const int n = blockIdx.x;
   const int64_t wg = static_cast<int64_t>(n & 7) * per_xcd + (n >> 3);
   const int64_t item = wg * 256 + threadIdx.x;
   if (item >= n_items) return;
   const int o8 = p.d_s / 8;
-  const int64_t bh = item / o8;
-  const int col = static_cast<int>(item % o8) * 8;
-  const int nblk = p.d_s / p.blk_cols;
-  const int b = static_cast<int>(bh / p.heads);
-  const int h = static_cast<int>(bh % p.heads);
-  const bool units = p.unit_table != nullptr;
-  const int2 ut = units ? reinterpret_cast<const int2*>(p.unit_table)[b] : make_int2(0, p.splits);
-  const int nsplit = ut.y;
-  // row of split s: a unit row, or the (split, sequence) row
-  const int64_t row_base = units ? static_cast<int64_t>(ut.x) * p.heads + h : bh;
-  const int64_t row_step = units ? p.heads : static_cast<int64_t>(p.batch) * p.heads;
-  const uint16_t* wh = reinterpret_cast<const uint16_t*>(p.ws_o);
-  const float* wsc = reinterpret_cast<const float*>(
-      reinterpret_cast<const char*>(p.ws_o) +
-      fp16_partials_scale_offset(p.splits, units ? 1 : p.batch, p.heads, p.d_s));
-  constexpr int kC = 16;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, tot = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += kC) {
-    float l[kC], f[kC];
-    uint4 v[kC];
-#pragma unroll
-    for (int u = 0; u < kC; ++u) {
-      const int64_t row = row_base + static_cast<int64_t>(min(s0 + u, nsplit - 1)) * row_step;
-      l[u] = p.ws_lse[row];
-      f[u] = wsc[row * nblk + col / p.blk_cols];
-      v[u] = *reinterpret_cast<const uint4*>(wh + row * p.d_s + col);
-    }
-    float cm = m;
-#pragma unroll
-    for (int u = 0; u < kC; ++u) {
-      if (s0 + u >= nsplit) l[u] = -INFINITY;
-      cm = fmaxf(cm, l[u]);
-    }
-    if (cm == -INFINITY) continue;              // no tokens so far
-    const float r = __expf(m - cm);             // 0 while m is still -inf
-    tot *= r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] *= r;
-#pragma unroll
-    for (int u = 0; u < kC; ++u) {
-      const bool use = l[u] != -INFINITY;       // empty splits: weight 0, o never used
-      const float w = use ? __expf(l[u] - cm) : 0.f;
-      tot += w;
-      const float wf = use ? w * f[u] : 0.f;
-      const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float h = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(wd[i >> 1] >> (16 * (i & 1)))));
-        acc[i] += use ? wf * h : 0.f;
-      }
-    }
-    m = cm;
-  }
-  float lse = -INFINITY;
-  if (m != -INFINITY) {
-    const float inv = 1.0f / tot;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] *= inv;
-    lse = m + __logf(tot);
-  }
-  const int64_t obase = b * p.out_sb + h * p.out_sh + col;
-  if constexpr (kBf16Out) {
-    uint16_t* o = static_cast<uint16_t*>(p.out) + obase;
-    if ((reinterpret_cast<uintptr_t>(o) & 15) == 0) {
-      uint32_t w[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        w[k] = static_cast<uint32_t>(f32_to_bf16(acc[2 * k])) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * k + 1])) << 16);
-      *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = f32_to_bf16(acc[i]);
-    }
+  int b, h, cb;
+  if constexpr (kUnits) {
+    h = static_cast<int>(item % p.heads);
+    const int64_t r = item / p.heads;
+    cb = static_cast<int>(r % o8);
+    b = static_cast<int>(r / o8);
   } else {
-    float* o = static_cast<float*>(p.out) + obase;
-    if ((reinterpret_cast<uintptr_t>(o) & 15) == 0) {
-      reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = acc[i];
-    }
+    const int64_t bh = item / o8;
+    cb = static_cast<int>(item % o8);
+    b = static_cast<int>(bh / p.heads);
+    h = static_cast<int>(bh % p.heads);
   }
-  if (p.lse != nullptr && col == 0) p.lse[bh] = lse;
+  const int2 ut = kUnits ? reinterpret_cast<const int2*>(p.unit_table)[b] : make_int2(0, p.splits);
+  merge16_item<kBf16Out, kUnits>(p, b, h, cb, ut);
 }
 
 template <typename TP, typename TO>
@@ -272,12 +207,16 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
     const int64_t items = static_cast<int64_t>(p.batch) * p.heads * (p.d_s / 8);
     const int64_t per_xcd = ((items + 255) / 256 + 7) / 8;
     if (8 * per_xcd > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (p.out_bf16)
-      hipLaunchKernelGGL((merge16_kernel<true>), dim3(static_cast<unsigned>(8 * per_xcd)), dim3(256), 0, s, p,
-                         items, static_cast<int>(per_xcd));
+    const dim3 grid(static_cast<unsigned>(8 * per_xcd));
+    const bool units = p.unit_table != nullptr;
+    if (p.out_bf16 && units)
+      hipLaunchKernelGGL((merge16_kernel<true, true>), grid, dim3(256), 0, s, p, items, static_cast<int>(per_xcd));
+    else if (p.out_bf16)
+      hipLaunchKernelGGL((merge16_kernel<true, false>), grid, dim3(256), 0, s, p, items, static_cast<int>(per_xcd));
+    else if (units)
+      hipLaunchKernelGGL((merge16_kernel<false, true>), grid, dim3(256), 0, s, p, items, static_cast<int>(per_xcd));
     else
-      hipLaunchKernelGGL((merge16_kernel<false>), dim3(static_cast<unsigned>(8 * per_xcd)), dim3(256), 0, s, p,
-                         items, static_cast<int>(per_xcd));
+      hipLaunchKernelGGL((merge16_kernel<false, false>), grid, dim3(256), 0, s, p, items, static_cast<int>(per_xcd));
     return hipGetLastError();
   }
   if (p.unit_table != nullptr) return hipErrorInvalidValue;   // unit rows come as fp16 only

@@ -1,0 +1,107 @@
+// The log-sum-exp merge of one (sequence b, head h, 8-column block cb) of
+// fp16 split outputs (o_s = scale_s * h_s, one scale per blk_cols columns):
+//     LSE = log sum_s exp(lse_s),   o = sum_s exp(lse_s - LSE) * o_s,
+// splits without tokens (lse_s = -inf) weighing 0.  Up to 16 splits per
+// memory round trip (every load of a chunk is issued before any is used),
+// with a running max across chunks.  Two layouts of the split outputs:
+//   rows (s, b, h) for s < splits, each [d_s] with scales [d_s / blk_cols];
+//   kUnits: sequence b owns units ut.x .. ut.x + ut.y - 1; unit u holds
+//     [d_s / 8][heads][8] halves and scales [d_s / blk_cols][heads], lse
+//     [heads].
+#pragma once
+
+#include "tpla_internal.h"
+
+namespace tpla {
+
+template <bool kBf16Out, bool kUnits>
+__device__ inline void merge16_item(const MergeParams& p, int b, int h, int cb, int2 ut) {
+  const int o8 = p.d_s / 8;
+  const int nblk = p.d_s / p.blk_cols;
+  const int col = cb * 8;
+  const int nsplit = ut.y;
+  const uint16_t* wh = reinterpret_cast<const uint16_t*>(p.ws_o);
+  const float* wsc = reinterpret_cast<const float*>(
+      reinterpret_cast<const char*>(p.ws_o) +
+      fp16_partials_scale_offset(p.splits, kUnits ? 1 : p.batch, p.heads, p.d_s));
+  constexpr int kC = 16;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, tot = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += kC) {
+    float l[kC], f[kC];
+    uint4 v[kC];
+#pragma unroll
+    for (int u = 0; u < kC; ++u) {
+      const int s = min(s0 + u, nsplit - 1);
+      if constexpr (kUnits) {
+        const int64_t unit = ut.x + s;
+        l[u] = p.ws_lse[unit * p.heads + h];
+        f[u] = wsc[(unit * nblk + col / p.blk_cols) * p.heads + h];
+        v[u] = *reinterpret_cast<const uint4*>(wh + ((unit * o8 + cb) * p.heads + h) * 8);
+      } else {
+        const int64_t row = static_cast<int64_t>(s) * p.batch * p.heads + static_cast<int64_t>(b) * p.heads + h;
+        l[u] = p.ws_lse[row];
+        f[u] = wsc[row * nblk + col / p.blk_cols];
+        v[u] = *reinterpret_cast<const uint4*>(wh + row * p.d_s + col);
+      }
+    }
+    float cm = m;
+#pragma unroll
+    for (int u = 0; u < kC; ++u) {
+      if (s0 + u >= nsplit) l[u] = -INFINITY;
+      cm = fmaxf(cm, l[u]);
+    }
+    if (cm == -INFINITY) continue;              // no tokens so far
+    const float r = __expf(m - cm);             // 0 while m is still -inf
+    tot *= r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= r;
+#pragma unroll
+    for (int u = 0; u < kC; ++u) {
+      const bool use = l[u] != -INFINITY;       // empty splits: weight 0, o never used
+      const float w = use ? __expf(l[u] - cm) : 0.f;
+      tot += w;
+      const float wf = use ? w * f[u] : 0.f;
+      const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float h = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(wd[i >> 1] >> (16 * (i & 1)))));
+        acc[i] += use ? wf * h : 0.f;
+      }
+    }
+    m = cm;
+  }
+  float lse = -INFINITY;
+  if (m != -INFINITY) {
+    const float inv = 1.0f / tot;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= inv;
+    lse = m + __logf(tot);
+  }
+  const int64_t obase = b * p.out_sb + h * p.out_sh + col;
+  if constexpr (kBf16Out) {
+    uint16_t* o = static_cast<uint16_t*>(p.out) + obase;
+    if ((reinterpret_cast<uintptr_t>(o) & 15) == 0) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = static_cast<uint32_t>(f32_to_bf16(acc[2 * k])) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * k + 1])) << 16);
+      *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = f32_to_bf16(acc[i]);
+    }
+  } else {
+    float* o = static_cast<float*>(p.out) + obase;
+    if ((reinterpret_cast<uintptr_t>(o) & 15) == 0) {
+      reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = acc[i];
+    }
+  }
+  if (p.lse != nullptr && col == 0) p.lse[static_cast<int64_t>(b) * p.heads + h] = lse;
+}
+
+}  // namespace tpla

@@ -140,7 +140,9 @@ struct Plan {
   bool units;
   int unit_target;
   int max_units;
+  size_t ws_o_off;       // split outputs
   size_t ws_o_bytes;
+  size_t lse_off;
   size_t table_off;      // unit table [batch][2] int32 (units only)
   size_t ws_bytes;
 };
@@ -201,8 +203,10 @@ tpla_status plan_decode(const tpla_decode_args* a, Plan* pl, int cus_given = 0) 
     }
     rows = static_cast<size_t>(pl->max_units) * a->heads;
   }
+  pl->ws_o_off = 0;
   pl->ws_o_bytes = round256(rows * a->d_s * sizeof(float));
-  pl->table_off = pl->ws_o_bytes + round256(rows * sizeof(float));
+  pl->lse_off = pl->ws_o_off + pl->ws_o_bytes;
+  pl->table_off = pl->lse_off + round256(rows * sizeof(float));
   pl->ws_bytes = pl->table_off + (pl->units ? round256(static_cast<size_t>(a->batch) * 8) : 0);
   return TPLA_OK;
 }
@@ -489,20 +493,12 @@ tpla_status launch_planned_decode(const tpla_decode_args* a, const Plan& pl, voi
   p.cache = a->cache;
   p.block_table = a->block_table;
   p.seq_lens = a->seq_lens;
-  p.ws_o = static_cast<float*>(workspace);
-  p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_o_bytes);
+  char* const ws = static_cast<char*>(workspace);
+  p.ws_o = reinterpret_cast<float*>(ws + pl.ws_o_off);
+  p.ws_lse = reinterpret_cast<float*>(ws + pl.lse_off);
   p.unit_target = pl.unit_target;
   p.max_units = pl.max_units;
-  p.unit_table = pl.units ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + pl.table_off)
-                          : nullptr;
-
-  hipError_t e;
-  switch (decode_path(a)) {
-    case Path::kStream: e = tpla::launch_decode_latsplit(p, s); break;
-    case Path::kMfma: e = tpla::launch_decode_mfma(p, s); break;
-    default: e = tpla::launch_decode_generic(p, a->dtype == TPLA_BF16, s); break;
-  }
-  if (e != hipSuccess) return hip_status(e, "decode launch");
+  p.unit_table = pl.units ? reinterpret_cast<int32_t*>(ws + pl.table_off) : nullptr;
 
   tpla::MergeParams m{};
   m.splits = pl.units ? pl.max_units : pl.splits;
@@ -521,6 +517,14 @@ tpla_status launch_planned_decode(const tpla_decode_args* a, const Plan& pl, voi
   m.out_sb = a->out_stride_b;
   m.out_sh = a->out_stride_h;
   m.lse = a->lse;
+
+  hipError_t e;
+  switch (decode_path(a)) {
+    case Path::kStream: e = tpla::launch_decode_latsplit(p, s); break;
+    case Path::kMfma: e = tpla::launch_decode_mfma(p, s); break;
+    default: e = tpla::launch_decode_generic(p, a->dtype == TPLA_BF16, s); break;
+  }
+  if (e != hipSuccess) return hip_status(e, "decode launch");
   return hip_status(tpla::launch_merge(m, s), "merge launch");
 }
 

@@ -35,6 +35,21 @@ template <> struct Elem<uint16_t> {
   __device__ __forceinline__ static void store(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 };
 
+struct MergeParams {
+  int splits, batch, heads, d_s;
+  int blk_cols;                 // 0: float32 partials; else fp16 partials, scale per blk_cols
+  // Non-null: the split outputs are rows [unit, heads] of `splits` units
+  // (batch 1 in the scale offset) and sequence b owns units
+  // unit_table[2b] .. unit_table[2b] + unit_table[2b+1] - 1.
+  const int32_t* unit_table;
+  const float* ws_o;
+  const float* ws_lse;
+  void* out;
+  int out_bf16;
+  int64_t out_sb, out_sh;
+  float* lse;
+};
+
 // ---------------------------------------------------------------------------
 // Decode kernel parameters (device pointers and sizes after validation).
 // ---------------------------------------------------------------------------
@@ -71,20 +86,6 @@ __host__ __device__ inline size_t fp16_partials_scale_offset(int splits, int bat
   return (n + 255) & ~static_cast<size_t>(255);
 }
 
-struct MergeParams {
-  int splits, batch, heads, d_s;
-  int blk_cols;                 // 0: float32 partials; else fp16 partials, scale per blk_cols
-  // Non-null: the split outputs are rows [unit, heads] of `splits` units
-  // (batch 1 in the scale offset) and sequence b owns units
-  // unit_table[2b] .. unit_table[2b] + unit_table[2b+1] - 1.
-  const int32_t* unit_table;
-  const float* ws_o;
-  const float* ws_lse;
-  void* out;
-  int out_bf16;
-  int64_t out_sb, out_sh;
-  float* lse;
-};
 
 constexpr int kMaxTp = 16;
 struct PartPtrs {

@@ -45,21 +45,17 @@ struct WorkUnit {
   int t0, t1;   // its tokens [t0, t1)
 };
 
-// Unit su of the map (call with the whole wave active; every argument
-// wave-uniform).  Returns false when su is past the last unit.  With
-// table != nullptr the wave also writes table[2b] = first_b and
-// table[2b + 1] = n_b for every sequence.
-__device__ inline bool find_unit(const DecodeParams& p, int su, int max_tiles, int32_t* table,
-                                 WorkUnit* w) {
-  const int lane = static_cast<int>(threadIdx.x & 63);
+// Clamped length of sequence b0 + lane (0 past the batch).
+__device__ __forceinline__ int unit_len(const DecodeParams& p, int b0) {
   const int cap = max(0, min(p.max_seq_len, p.max_blocks * p.block_size));
-  auto len_at = [&](int b0) -> int {
-    const int b = b0 + lane;
-    return b < p.batch ? max(0, min(p.seq_lens[b], cap)) : 0;
-  };
-  const int len0 = len_at(0);                 // the first 64 sequences stay in a register
-  auto len_of = [&](int b0) -> int { return b0 == 0 ? len0 : len_at(b0); };
+  const int b = b0 + static_cast<int>(threadIdx.x & 63);
+  return b < p.batch ? max(0, min(p.seq_lens[b], cap)) : 0;
+}
 
+// The chunk c of the map, in tiles (wave-uniform; len_of(b0) gives the
+// lengths of sequences b0 + lane).
+template <typename LenOf>
+__device__ inline int unit_chunk(const DecodeParams& p, int max_tiles, LenOf len_of) {
   int c;
   if (p.unit_target > 0) {
     const int n_target = p.unit_target;
@@ -88,7 +84,19 @@ __device__ inline bool find_unit(const DecodeParams& p, int su, int max_tiles, i
   } else {
     c = max(1, p.chunk >> 6);
   }
-  c = min(c, max_tiles);
+  return min(c, max_tiles);
+}
+
+// Unit su of the map (call with the whole wave active; every argument
+// wave-uniform).  Returns false when su is past the last unit.  With
+// table != nullptr the wave also writes table[2b] = first_b and
+// table[2b + 1] = n_b for every sequence.
+__device__ inline bool find_unit(const DecodeParams& p, int su, int max_tiles, int32_t* table,
+                                 WorkUnit* w) {
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  const int len0 = unit_len(p, 0);            // the first 64 sequences stay in a register
+  auto len_of = [&](int b0) -> int { return b0 == 0 ? len0 : unit_len(p, b0); };
+  const int c = unit_chunk(p, max_tiles, len_of);
 
   bool found = false;
   WorkUnit r{0, 0, 0};
