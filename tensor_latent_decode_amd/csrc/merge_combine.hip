@@ -145,10 +145,14 @@ __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_i
   const int o8 = p.d_s / 8;
   int b, h, cb;
   if constexpr (kUnits) {
-    h = static_cast<int>(item % p.heads);
-    const int64_t r = item / p.heads;
-    cb = static_cast<int>(r % o8);
-    b = static_cast<int>(r / o8);
+    // a wavefront takes 8 heads x 8 column blocks: reads in 128-byte runs
+    // (8 heads of one block), writes in runs of 8 blocks of one head
+    const int64_t per_seq = static_cast<int64_t>(o8) * p.heads;
+    b = static_cast<int>(item / per_seq);
+    const int r = static_cast<int>(item % per_seq);
+    const int rest = r >> 6;
+    h = (rest % (p.heads / 8)) * 8 + (r & 7);
+    cb = (rest / (p.heads / 8)) * 8 + ((r >> 3) & 7);
   } else {
     const int64_t bh = item / o8;
     cb = static_cast<int>(item % o8);
@@ -203,6 +207,8 @@ void launch_m(const MergeParams& p, int64_t n_items, int64_t per_xcd, hipStream_
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
+  // unit rows: waves of 8 heads x 8 column blocks
+  if (p.unit_table != nullptr && (p.heads % 8 != 0 || (p.d_s / 8) % 8 != 0)) return hipErrorInvalidValue;
   if (p.blk_cols != 0 && p.blk_cols % 8 == 0 && p.d_s % p.blk_cols == 0) {
     const int64_t items = static_cast<int64_t>(p.batch) * p.heads * (p.d_s / 8);
     const int64_t per_xcd = ((items + 255) / 256 + 7) / 8;
