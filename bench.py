@@ -94,7 +94,7 @@ def kernel_source_hash() -> str:
     csrc = os.path.join(ROOT, "tensor_latent_decode_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.startswith("decode_") or name in ("tpla_api.hip", "merge_combine.hip",
-                                                  "tpla_internal.h", "unit_map.h"):
+                                                  "tpla_internal.h", "unit_map.h", "merge_item.h"):
             h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
