@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libtpla.so")
 
 SOURCES = ["tpla_api.hip", "hadamard.hip", "append.hip", "decode_generic.hip",
            "decode_mfma.hip", "decode_latsplit.hip", "decode_roles.hip", "decode_mla.hip",
-           "merge_combine.hip", "up_project.hip", "mla_prefill.hip"]
+           "merge_combine.hip", "up_project.hip", "mla_prefill.hip", "prefill_roles.hip"]
 
 # gfx950 only.  Packed fp32 vector ops are switched off for all device code.
 HIPCC_FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC",

@@ -642,7 +642,10 @@ tpla_status tpla_mla_prefill(const tpla_prefill_args* a, void* stream) {
   p.o_s = a->out_stride_t;
   p.o_h = a->out_stride_h;
   p.lse = a->lse;
-  return hip_status(tpla::launch_mla_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(tpla::prefill_roles_supported(p.heads, p.kv_s) ? tpla::launch_prefill_roles(p, s)
+                                                                    : tpla::launch_mla_prefill(p, s),
+                    "prefill launch");
 }
 
 tpla_status tpla_up_project(const void* o, tpla_dtype o_dtype, int64_t o_stride_b,

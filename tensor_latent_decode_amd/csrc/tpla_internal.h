@@ -156,6 +156,8 @@ struct PrefillParams {
 
 // Launchers (return the launch status; they do not synchronise).
 hipError_t launch_mla_prefill(const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill_roles(const PrefillParams& p, hipStream_t s);
+bool prefill_roles_supported(int heads, int64_t kv_stride_t);
 hipError_t launch_up_project(const UpProjectParams& p, bool o_bf16, bool w_bf16, bool y_bf16,
                              hipStream_t s);
 hipError_t launch_hadamard(const void* x, int x_bf16, int64_t xs, void* y, int y_bf16, int64_t ys,

@@ -1002,8 +1002,9 @@ def test_prefill_late_score_spike():
     assert np.max(np.abs(lse[0] - ref_l)) <= 2e-2
 
 
-def test_prefill_strided_buffers_give_the_same_bits():
-    pc = make_prefill_case(PREFILL_CONFIGS["prefill_small"], heads=16, seed=97)
+@pytest.mark.parametrize("heads", [16, 64])
+def test_prefill_strided_buffers_give_the_same_bits(heads):
+    pc = make_prefill_case(PREFILL_CONFIGS["prefill_small"], heads=heads, seed=97)
     B, S, H, d_c = pc.q_latent.shape
     base, _ = run_prefill(pc)
     wq = torch.zeros((B, S, H, 640), dtype=torch.bfloat16, device="cuda")
@@ -1019,6 +1020,22 @@ def test_prefill_strided_buffers_give_the_same_bits():
     got = host_f64(wout)
     assert np.array_equal(got[..., :512], base)
     assert np.all(got[..., 512:] == SENTINEL)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.06])
+def test_prefill_zero_and_negative_scale(scale):
+    """A zero scale weighs every visible key equally; a negative one flips the
+    scores (64 heads: the role-split kernel's sign and zero handling)."""
+    from dataclasses import replace
+    pc = make_prefill_case(PREFILL_CONFIGS["prefill_small"], batch=2, heads=64, lens=140,
+                           max_len=140, seed=99)
+    pc.cfg = replace(pc.cfg, scale=scale)
+    out, lse = run_prefill(pc)
+    for b in range(2):
+        L = int(pc.seq_lens[b])
+        ref_o, ref_l = prefill_ref(pc, b)
+        assert rel_err(out[b, :L], ref_o) <= TOL_BF16, (b, scale)
+        assert np.max(np.abs(lse[b, :L] - ref_l)) <= 2e-2, (b, scale)
 
 
 def test_prefill_4k_sampled():
