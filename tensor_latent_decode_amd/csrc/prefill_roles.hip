@@ -364,8 +364,8 @@ void prefill_roles_kernel(PrefillParams p, int n_units) {
   bf16x8_t vc[kMPW][4];        // V^T fragments of the tile whose values are due
 
   // Values of tile i (V^T in vc, P^T in ptile[i % 2]); with kNext, V^T of
-  // tile i+1 is read into vc right after each fragment's last use and the
-  // copy of tile i+2 (when there is one) is spread over the MFMAs.
+  // tile i+1 is read into vc right after each fragment's last use, and the
+  // copy of tile i+2 (when there is one) is issued first.
   auto values = [&](int i, auto next_c) {
     constexpr bool kNext = decltype(next_c)::value;
     const bool do_copy = kNext && i + 2 < ntiles;
@@ -374,6 +374,12 @@ void prefill_roles_kernel(PrefillParams p, int n_units) {
     auto frag = [&](int f) -> bf16x8_t {      // f = j * 2 + ht
       return __builtin_bit_cast(bf16x8_t, P[((f & 1) * 4 + (f >> 1)) * 64 + lane]);
     };
+    // the copy goes out first: a whole step to land (the tile is mostly
+    // in the L2, where spreading the copies over the MFMAs only delays them)
+    if (do_copy) {
+#pragma unroll
+      for (int k = 0; k < kIPT; ++k) copy_chunk(i + 2, k);
+    }
     bf16x8_t pa[kPPre];
 #pragma unroll
     for (int f = 0; f < kPPre; ++f) pa[f] = frag(f);
@@ -387,11 +393,6 @@ void prefill_roles_kernel(PrefillParams p, int n_units) {
       if (kNext && ht == 1) {
 #pragma unroll
         for (int mm = 0; mm < kMPW; ++mm) vc[mm][j] = rd_v(Tn, mm, j);
-      }
-      if (do_copy) {
-#pragma unroll
-        for (int k = 0; k < kIPT; ++k)
-          if ((k * 8) / kIPT == f) copy_chunk(i + 2, k);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
