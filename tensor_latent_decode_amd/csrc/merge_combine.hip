@@ -11,8 +11,10 @@
 // Combine: shard g owns latent columns g*d_s .. (g+1)*d_s, so summing the
 // zero-padded shard outputs (the all-reduce of the TPLA abstract) places
 // them side by side.
-#include "tpla_internal.h"
+#include <type_traits>
+
 #include "merge_item.h"
+#include "tpla_internal.h"
 
 namespace tpla {
 namespace {
@@ -136,12 +138,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_ite
 //     table); unit u holds [d_s / 8][heads][8] halves and scales
 //     [d_s / blk_cols][heads]: threads take the heads fastest, so a
 //     wavefront reads 1 KB of one unit at a time.
-template <bool kBf16Out, bool kUnits>
+template <bool kBf16Out, bool kUnits, int G>
 __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_items, int per_xcd) {
   const int n = blockIdx.x;
   const int64_t wg = static_cast<int64_t>(n & 7) * per_xcd + (n >> 3);
-  const int64_t item = wg * 256 + threadIdx.x;
-  if (item >= n_items) return;
+  const int64_t tid = wg * 256 + threadIdx.x;
+  const int64_t item = tid / G;                 // G lanes per item (a power of two dividing 256)
+  const int g = static_cast<int>(tid % G);
+  if (item >= n_items) return;                  // whole groups leave together
   const int o8 = p.d_s / 8;
   int b, h, cb;
   if constexpr (kUnits) {
@@ -160,7 +164,9 @@ __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_i
     h = static_cast<int>(bh % p.heads);
   }
   const int2 ut = kUnits ? reinterpret_cast<const int2*>(p.unit_table)[b] : make_int2(0, p.splits);
-  merge16_item<kBf16Out, kUnits>(p, b, h, cb, ut);
+  MergePart r = merge16_partial<kUnits>(p, b, h, cb, ut, g, G);
+  merge_lanes(r, G);
+  if (g == 0) merge16_store<kBf16Out>(p, b, h, cb, r);
 }
 
 template <typename TP, typename TO>
@@ -211,18 +217,32 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
   if (p.unit_table != nullptr && (p.heads % 8 != 0 || (p.d_s / 8) % 8 != 0)) return hipErrorInvalidValue;
   if (p.blk_cols != 0 && p.blk_cols % 8 == 0 && p.d_s % p.blk_cols == 0) {
     const int64_t items = static_cast<int64_t>(p.batch) * p.heads * (p.d_s / 8);
-    const int64_t per_xcd = ((items + 255) / 256 + 7) / 8;
+    const bool units = p.unit_table != nullptr;
+    // lanes per item: past 16 splits (two memory round trips for one lane)
+    // about 8 splits per lane, so the item takes one round trip and more
+    // waves are in flight (unit rows: one lane; their count per sequence is
+    // known only on the device)
+    int G = 1;
+    if (!units && p.splits > 16)
+      while (G < 8 && G * 8 < p.splits) G *= 2;
+    const int64_t per_xcd = ((items * G + 255) / 256 + 7) / 8;
     if (8 * per_xcd > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(8 * per_xcd));
-    const bool units = p.unit_table != nullptr;
-    if (p.out_bf16 && units)
-      hipLaunchKernelGGL((merge16_kernel<true, true>), grid, dim3(256), 0, s, p, items, static_cast<int>(per_xcd));
-    else if (p.out_bf16)
-      hipLaunchKernelGGL((merge16_kernel<true, false>), grid, dim3(256), 0, s, p, items, static_cast<int>(per_xcd));
-    else if (units)
-      hipLaunchKernelGGL((merge16_kernel<false, true>), grid, dim3(256), 0, s, p, items, static_cast<int>(per_xcd));
-    else
-      hipLaunchKernelGGL((merge16_kernel<false, false>), grid, dim3(256), 0, s, p, items, static_cast<int>(per_xcd));
+    const int px = static_cast<int>(per_xcd);
+    if (units) {
+      if (p.out_bf16) hipLaunchKernelGGL((merge16_kernel<true, true, 1>), grid, dim3(256), 0, s, p, items, px);
+      else hipLaunchKernelGGL((merge16_kernel<false, true, 1>), grid, dim3(256), 0, s, p, items, px);
+    } else {
+      auto go = [&](auto g_c) {
+        constexpr int kG = decltype(g_c)::value;
+        if (p.out_bf16) hipLaunchKernelGGL((merge16_kernel<true, false, kG>), grid, dim3(256), 0, s, p, items, px);
+        else hipLaunchKernelGGL((merge16_kernel<false, false, kG>), grid, dim3(256), 0, s, p, items, px);
+      };
+      if (G == 1) go(std::integral_constant<int, 1>());
+      else if (G == 2) go(std::integral_constant<int, 2>());
+      else if (G == 4) go(std::integral_constant<int, 4>());
+      else go(std::integral_constant<int, 8>());
+    }
     return hipGetLastError();
   }
   if (p.unit_table != nullptr) return hipErrorInvalidValue;   // unit rows come as fp16 only

@@ -3,7 +3,10 @@
 //     LSE = log sum_s exp(lse_s),   o = sum_s exp(lse_s - LSE) * o_s,
 // splits without tokens (lse_s = -inf) weighing 0.  Up to 16 splits per
 // memory round trip (every load of a chunk is issued before any is used),
-// with a running max across chunks.  Two layouts of the split outputs:
+// with a running max across chunks.  The splits of an item may be shared by
+// G adjacent lanes (lane g takes splits g, g + G, ...), whose partial
+// results then combine exactly the same way across the lanes.  Two layouts
+// of the split outputs:
 //   rows (s, b, h) for s < splits, each [d_s] with scales [d_s / blk_cols];
 //   kUnits: sequence b owns units ut.x .. ut.x + ut.y - 1; unit u holds
 //     [d_s / 8][heads][8] halves and scales [d_s / blk_cols][heads], lse
@@ -14,8 +17,14 @@
 
 namespace tpla {
 
-template <bool kBf16Out, bool kUnits>
-__device__ inline void merge16_item(const MergeParams& p, int b, int h, int cb, int2 ut) {
+struct MergePart {
+  float m, tot;        // running max and sum of exp(lse_s - m)
+  float acc[8];        // sum of exp(lse_s - m) * o_s, 8 columns
+};
+
+template <bool kUnits>
+__device__ inline MergePart merge16_partial(const MergeParams& p, int b, int h, int cb, int2 ut, int g,
+                                            int G) {
   const int o8 = p.d_s / 8;
   const int nblk = p.d_s / p.blk_cols;
   const int col = cb * 8;
@@ -25,14 +34,17 @@ __device__ inline void merge16_item(const MergeParams& p, int b, int h, int cb, 
       reinterpret_cast<const char*>(p.ws_o) +
       fp16_partials_scale_offset(p.splits, kUnits ? 1 : p.batch, p.heads, p.d_s));
   constexpr int kC = 16;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, tot = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += kC) {
+  MergePart r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.acc[i] = 0.f;
+  r.m = -INFINITY;
+  r.tot = 0.f;
+  for (int s0 = g; s0 < nsplit; s0 += kC * G) {
     float l[kC], f[kC];
     uint4 v[kC];
 #pragma unroll
     for (int u = 0; u < kC; ++u) {
-      const int s = min(s0 + u, nsplit - 1);
+      const int s = min(s0 + u * G, nsplit - 1);
       if constexpr (kUnits) {
         const int64_t unit = ut.x + s;
         l[u] = p.ws_lse[unit * p.heads + h];
@@ -45,39 +57,64 @@ __device__ inline void merge16_item(const MergeParams& p, int b, int h, int cb, 
         v[u] = *reinterpret_cast<const uint4*>(wh + row * p.d_s + col);
       }
     }
-    float cm = m;
+    float cm = r.m;
 #pragma unroll
     for (int u = 0; u < kC; ++u) {
-      if (s0 + u >= nsplit) l[u] = -INFINITY;
+      if (s0 + u * G >= nsplit) l[u] = -INFINITY;
       cm = fmaxf(cm, l[u]);
     }
     if (cm == -INFINITY) continue;              // no tokens so far
-    const float r = __expf(m - cm);             // 0 while m is still -inf
-    tot *= r;
+    const float sc = __expf(r.m - cm);          // 0 while m is still -inf
+    r.tot *= sc;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] *= r;
+    for (int i = 0; i < 8; ++i) r.acc[i] *= sc;
 #pragma unroll
     for (int u = 0; u < kC; ++u) {
       const bool use = l[u] != -INFINITY;       // empty splits: weight 0, o never used
       const float w = use ? __expf(l[u] - cm) : 0.f;
-      tot += w;
+      r.tot += w;
       const float wf = use ? w * f[u] : 0.f;
       const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float h = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(wd[i >> 1] >> (16 * (i & 1)))));
-        acc[i] += use ? wf * h : 0.f;
+        const float hv = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(wd[i >> 1] >> (16 * (i & 1)))));
+        r.acc[i] += use ? wf * hv : 0.f;
       }
     }
-    m = cm;
+    r.m = cm;
   }
-  float lse = -INFINITY;
-  if (m != -INFINITY) {
-    const float inv = 1.0f / tot;
+  return r;
+}
+
+// Combines the partials of G adjacent lanes (G a power of two, the group
+// aligned to G); every lane of the group ends with the whole.
+__device__ inline void merge_lanes(MergePart& r, int G) {
+  for (int off = 1; off < G; off <<= 1) {
+    const float m_o = __shfl_xor(r.m, off);
+    const float t_o = __shfl_xor(r.tot, off);
+    float a_o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] *= inv;
-    lse = m + __logf(tot);
+    for (int i = 0; i < 8; ++i) a_o[i] = __shfl_xor(r.acc[i], off);
+    const float mm = fmaxf(r.m, m_o);
+    if (mm == -INFINITY) continue;              // neither has tokens
+    const float s1 = __expf(r.m - mm), s2 = __expf(m_o - mm);   // 0 for a side at -inf
+    r.tot = r.tot * s1 + t_o * s2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.acc[i] = r.acc[i] * s1 + a_o[i] * s2;
+    r.m = mm;
   }
+}
+
+// o = acc / tot and LSE = m + log tot (0 and -inf without tokens).
+template <bool kBf16Out>
+__device__ inline void merge16_store(const MergeParams& p, int b, int h, int cb, const MergePart& r) {
+  const int col = cb * 8;
+  float acc[8];
+  float lse = -INFINITY;
+  const float inv = r.m != -INFINITY ? 1.0f / r.tot : 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = r.acc[i] * inv;
+  if (r.m != -INFINITY) lse = r.m + __logf(r.tot);
   const int64_t obase = b * p.out_sb + h * p.out_sh + col;
   if constexpr (kBf16Out) {
     uint16_t* o = static_cast<uint16_t*>(p.out) + obase;
