@@ -635,9 +635,9 @@ int decode_latsplit_max_chunk() { return min(kMaxTiles * kTile, decode_mla_max_c
 
 int decode_latsplit_partial_block() { return 64; }
 
-// Instantiations: 128-head groups with d_s = 256 (four waves, three K
-// buffers, one workgroup per CU) and 64-head groups with d_s = 128 (two
-// waves, two K buffers, two workgroups per CU); both with d_r = 64.
+// Instantiated for 64-head groups with d_s = 128, d_r = 64 (two waves, two
+// K buffers, two workgroups per CU).  128-head groups with d_s = 256 go to
+// the kernel with separate score and value waves in decode_roles.hip.
 // The 512-wide latent (plain MLA under tensor parallelism, or a one-shard
 // TPLA) goes to the kernel in decode_mla.hip, which keeps the same split
 // output format.
@@ -661,7 +661,6 @@ hipError_t launch_decode_latsplit(const DecodeParams& p, hipStream_t s) {
   if (!decode_latsplit_supported(p.heads, p.d_s, p.d_r, p.block_size)) return hipErrorNotSupported;
   if (decode_mla_supported(p.heads, p.d_s, p.d_r, p.block_size)) return launch_decode_mla(p, s);
   if (decode_roles_supported(p.heads, p.d_s, p.d_r, p.block_size)) return launch_decode_roles(p, s);
-  if (p.heads % 128 == 0 && p.d_s == 256) return launch_t<4, 256, 64, 3>(p, s);
   return launch_t<2, 128, 64, 2>(p, s);
 }
 

@@ -261,10 +261,6 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   float* const part_sc = reinterpret_cast<float*>(reinterpret_cast<char*>(p.ws_o) +
                                                   fp16_partials_scale_offset(p.max_units, 1, p.heads, DS)) +
                          row0 * (DS / 64);
-  // With the merge inside the launch: once every wave's writes of this
-  // unit have reached the L2 (each wave waits for its own stores), one
-  // release by one thread (an L2 write-back) publishes them all and counts
-  // the unit in for its sequence.
 
   if (is_score) {
     // =====================================================================
