@@ -438,31 +438,71 @@ void prefill_roles_kernel(PrefillParams p, int n_units) {
   }
   barrier();                                      // B_l: row sums in lsum
 
-  // o = U / l straight from the accumulators: register r of latent tile
-  // 4lq + mm holds column 32(4lq + mm) + 8(r/4) + 4half + r%4 of head
-  // 32ht + l31
+  // o = U / l: register r of latent tile 4lq + mm holds column
+  // 32(4lq + mm) + 8(r/4) + 4half + r%4 of head 32ht + l31, so a lane owns
+  // 8- or 16-byte pieces of 32 different rows.  Stored as they are, every
+  // store instruction touches 32 rows; instead each head tile goes through
+  // LDS (K buffer 1, idle once the last values are done; wave lq owns 32
+  // rows x 128 columns of it, 16-byte chunk c of row r at chunk c ^ (r & 15),
+  // which keeps both the writes and the reads free of bank conflicts) and
+  // comes back as whole 16-byte chunks: one store instruction then writes
+  // 4 (bf16) or 2 (float) contiguous 256- or 512-byte row pieces.  Rows that
+  // are not 16-byte aligned take the direct stores.
+  constexpr int kEs = kOutBf16 ? 2 : 4;      // output element bytes
+  constexpr int kRB = 128 * kEs;             // bytes of a wave's piece of one row
+  constexpr int kNC = kRB / 16;              // its 16-byte chunks
+  auto row_ptr = [&](int head) -> char* {
+    return static_cast<char*>(p.out) +
+           (b * p.o_b + static_cast<int64_t>(t) * p.o_s + static_cast<int64_t>(head) * p.o_h) * kEs;
+  };
+  const bool staged =
+      ((reinterpret_cast<uintptr_t>(p.out) | static_cast<uint64_t>(p.o_b | p.o_s | p.o_h) * kEs) & 15) == 0;
+  char* const stage = reinterpret_cast<char*>(&ktile[1][0]) + lq * 32 * kRB;
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
-    const int head = head0 + ht * 32 + l31;
     const float inv_l = 1.0f / lsum[ht * 32 + l31];
-    char* orow = static_cast<char*>(p.out) +
-                 (b * p.o_b + static_cast<int64_t>(t) * p.o_s + static_cast<int64_t>(head) * p.o_h) *
-                     (kOutBf16 ? 2 : 4);
+    if (staged) {
 #pragma unroll
-    for (int mm = 0; mm < kMPW; ++mm)
+      for (int mm = 0; mm < kMPW; ++mm)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int col = 32 * (kMPW * lq + mm) + 8 * q4 + 4 * half;
-        const float v0 = oacc[mm][ht][4 * q4] * inv_l, v1 = oacc[mm][ht][4 * q4 + 1] * inv_l;
-        const float v2 = oacc[mm][ht][4 * q4 + 2] * inv_l, v3 = oacc[mm][ht][4 * q4 + 3] * inv_l;
-        if constexpr (kOutBf16) {
-          const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
-          const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(v2)) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
-          *reinterpret_cast<uint2*>(orow + col * 2) = make_uint2(w0, w1);
-        } else {
-          *reinterpret_cast<float4*>(orow + col * 4) = make_float4(v0, v1, v2, v3);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float v0 = oacc[mm][ht][4 * q4] * inv_l, v1 = oacc[mm][ht][4 * q4 + 1] * inv_l;
+          const float v2 = oacc[mm][ht][4 * q4 + 2] * inv_l, v3 = oacc[mm][ht][4 * q4 + 3] * inv_l;
+          const int cbyte = (32 * mm + 8 * q4 + 4 * half) * kEs;   // byte of the wave's row piece
+          char* dst = stage + l31 * kRB + (((cbyte >> 4) ^ (l31 & 15)) << 4) + (cbyte & 15);
+          if constexpr (kOutBf16) {
+            const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
+            const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(v2)) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
+          }
         }
+#pragma unroll
+      for (int k = 0; k < 32 * kNC / 64; ++k) {
+        const int idx = k * 64 + lane;
+        const int r = idx / kNC, cc = idx % kNC;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + r * kRB + ((cc ^ (r & 15)) << 4));
+        *reinterpret_cast<uint4*>(row_ptr(head0 + ht * 32 + r) + lq * kRB + cc * 16) = v;
       }
+    } else {
+      char* const orow = row_ptr(head0 + ht * 32 + l31);
+#pragma unroll
+      for (int mm = 0; mm < kMPW; ++mm)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int col = 32 * (kMPW * lq + mm) + 8 * q4 + 4 * half;
+          const float v0 = oacc[mm][ht][4 * q4] * inv_l, v1 = oacc[mm][ht][4 * q4 + 1] * inv_l;
+          const float v2 = oacc[mm][ht][4 * q4 + 2] * inv_l, v3 = oacc[mm][ht][4 * q4 + 3] * inv_l;
+          if constexpr (kOutBf16) {
+            const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
+            const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(v2)) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
+            *reinterpret_cast<uint2*>(orow + col * 2) = make_uint2(w0, w1);
+          } else {
+            *reinterpret_cast<float4*>(orow + col * 4) = make_float4(v0, v1, v2, v3);
+          }
+        }
+    }
   }
 }
 

@@ -10,19 +10,15 @@ namespace tpla {
 
 // ---------------------------------------------------------------------------
 // bf16 <-> float32 on the device.  bf16 values travel as uint16_t bit
-// patterns; conversions to bf16 round to nearest, ties to even.
+// patterns; conversions to bf16 round to nearest, ties to even (the
+// hardware conversion: no branch per value, a NaN stays a quiet NaN).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u) {
-    return static_cast<uint16_t>((u >> 16) | 0x0040u);  // quiet NaN, sign kept
-  }
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));   // v_cvt_pk_bf16_f32: RNE
 }
 
 template <typename T> struct Elem;

@@ -1022,6 +1022,24 @@ def test_prefill_strided_buffers_give_the_same_bits(heads):
     assert np.all(got[..., 512:] == SENTINEL)
 
 
+@pytest.mark.parametrize("out_dt,width", [(torch.float32, 516), (torch.bfloat16, 520), (torch.bfloat16, 516)])
+def test_prefill_output_rows_aligned_or_not_give_the_same_bits(out_dt, width):
+    """Output rows whose byte stride is a multiple of 16 (float 516, bf16 520
+    wide) go out as whole 16-byte chunks, a bf16 stride of 516 (8-byte
+    aligned, which the call accepts) as 8-byte pieces; both give the bits of
+    the packed output and leave the row padding alone."""
+    pc = make_prefill_case(PREFILL_CONFIGS["prefill_small"], heads=64, seed=98)
+    B, S, H, d_c = pc.q_latent.shape
+    base, _ = run_prefill(pc, out_dtype=out_dt)
+    wout = torch.full((B, S, H, width), SENTINEL, dtype=out_dt, device="cuda")
+    tpla.mla_prefill(dev(pc.q_latent), dev(pc.q_rope), dev(pc.kv), dev(pc.seq_lens), pc.cfg.scale,
+                     out=wout[..., :512])
+    torch.cuda.synchronize()
+    got = host_f64(wout)
+    assert np.array_equal(got[..., :512], base)
+    assert np.all(got[..., 512:] == host_f64(torch.full((1,), SENTINEL, dtype=out_dt))[0])
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.06])
 def test_prefill_zero_and_negative_scale(scale):
     """A zero scale weighs every visible key equally; a negative one flips the
