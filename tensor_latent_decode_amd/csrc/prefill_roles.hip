@@ -124,6 +124,13 @@ __device__ __forceinline__ float both_halves_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Two floats to packed bf16 (round to nearest even) in one instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 using kTrue_t = std::integral_constant<bool, true>;
 using kFalse_t = std::integral_constant<bool, false>;
 constexpr kTrue_t kTrue{};
@@ -471,9 +478,7 @@ void prefill_roles_kernel(PrefillParams p, int n_units) {
           const int cbyte = (32 * mm + 8 * q4 + 4 * half) * kEs;   // byte of the wave's row piece
           char* dst = stage + l31 * kRB + (((cbyte >> 4) ^ (l31 & 15)) << 4) + (cbyte & 15);
           if constexpr (kOutBf16) {
-            const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
-            const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(v2)) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
-            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
           } else {
             *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
           }
@@ -495,9 +500,7 @@ void prefill_roles_kernel(PrefillParams p, int n_units) {
           const float v0 = oacc[mm][ht][4 * q4] * inv_l, v1 = oacc[mm][ht][4 * q4 + 1] * inv_l;
           const float v2 = oacc[mm][ht][4 * q4 + 2] * inv_l, v3 = oacc[mm][ht][4 * q4 + 3] * inv_l;
           if constexpr (kOutBf16) {
-            const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
-            const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(v2)) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
-            *reinterpret_cast<uint2*>(orow + col * 2) = make_uint2(w0, w1);
+            *reinterpret_cast<uint2*>(orow + col * 2) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
           } else {
             *reinterpret_cast<float4*>(orow + col * 4) = make_float4(v0, v1, v2, v3);
           }
