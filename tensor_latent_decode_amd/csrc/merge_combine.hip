@@ -157,13 +157,21 @@ __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_i
     const int rest = r >> 6;
     h = (rest % (p.heads / 8)) * 8 + (r & 7);
     cb = (rest / (p.heads / 8)) * 8 + ((r >> 3) & 7);
+    // per_seq is a multiple of 64 (heads % 8 == 0, d_s / 8 % 8 == 0): one
+    // sequence per wavefront, whose unit range comes by a scalar load
+    b = __builtin_amdgcn_readfirstlane(b);
   } else {
     const int64_t bh = item / o8;
     cb = static_cast<int>(item % o8);
     b = static_cast<int>(bh / p.heads);
     h = static_cast<int>(bh % p.heads);
   }
-  const int2 ut = kUnits ? reinterpret_cast<const int2*>(p.unit_table)[b] : make_int2(0, p.splits);
+  int2 ut = make_int2(0, p.splits);
+  if constexpr (kUnits) {
+    typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+    const const_i32_t* e = (const const_i32_t*)(p.unit_table + 2 * static_cast<int64_t>(b));
+    ut = make_int2(e[0], e[1]);
+  }
   MergePart r = merge16_partial<kUnits>(p, b, h, cb, ut, g, G);
   merge_lanes(r, G);
   if (g == 0) merge16_store<kBf16Out>(p, b, h, cb, r);
