@@ -492,7 +492,9 @@ typedef struct tpla_prefill_args {
  * Layout: q_latent, q_rope and kv 16-byte aligned with strides that are
  * multiples of 8 elements; out 16-byte aligned with strides that are
  * multiples of 4 elements; kv_stride_t >= d_c + d_r and below 2^26.
- * Kernel: bf16 matrix cores, 64 (position, head) rows per workgroup.
+ * Kernel: bf16 matrix cores.  With heads a multiple of 64, one workgroup of
+ * eight waves per (prompt, position, 64 heads), score and value waves
+ * apart; otherwise one workgroup of four waves per 64 (position, head) rows.
  * Errors: TPLA_ERR_NULL, TPLA_ERR_SHAPE, TPLA_ERR_ALIGN, TPLA_ERR_DTYPE,
  * TPLA_ERR_UNSUPPORTED (d_c != 512 or d_r != 64), TPLA_ERR_HIP.
  */
