@@ -228,29 +228,31 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
     const bool units = p.unit_table != nullptr;
     // lanes per item: past 16 splits (two memory round trips for one lane)
     // about 8 splits per lane, so the item takes one round trip and more
-    // waves are in flight (unit rows: one lane; their count per sequence is
-    // known only on the device)
+    // waves are in flight.  Unit rows: their count per sequence is known
+    // only on the device; the launch's average (max_units / batch) decides,
+    // which is exact for uniform lengths and only a rate choice otherwise
+    const int per_seq = units ? (p.splits + p.batch - 1) / p.batch : p.splits;
     int G = 1;
-    if (!units && p.splits > 16)
-      while (G < 8 && G * 8 < p.splits) G *= 2;
+    if (per_seq > 16)
+      while (G < 8 && G * 8 < per_seq) G *= 2;
     const int64_t per_xcd = ((items * G + 255) / 256 + 7) / 8;
     if (8 * per_xcd > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(8 * per_xcd));
     const int px = static_cast<int>(per_xcd);
-    if (units) {
-      if (p.out_bf16) hipLaunchKernelGGL((merge16_kernel<true, true, 1>), grid, dim3(256), 0, s, p, items, px);
-      else hipLaunchKernelGGL((merge16_kernel<false, true, 1>), grid, dim3(256), 0, s, p, items, px);
-    } else {
-      auto go = [&](auto g_c) {
-        constexpr int kG = decltype(g_c)::value;
-        if (p.out_bf16) hipLaunchKernelGGL((merge16_kernel<true, false, kG>), grid, dim3(256), 0, s, p, items, px);
-        else hipLaunchKernelGGL((merge16_kernel<false, false, kG>), grid, dim3(256), 0, s, p, items, px);
-      };
-      if (G == 1) go(std::integral_constant<int, 1>());
-      else if (G == 2) go(std::integral_constant<int, 2>());
-      else if (G == 4) go(std::integral_constant<int, 4>());
-      else go(std::integral_constant<int, 8>());
-    }
+    auto go = [&](auto units_c, auto g_c) {
+      constexpr bool kU = decltype(units_c)::value;
+      constexpr int kG = decltype(g_c)::value;
+      if (p.out_bf16) hipLaunchKernelGGL((merge16_kernel<true, kU, kG>), grid, dim3(256), 0, s, p, items, px);
+      else hipLaunchKernelGGL((merge16_kernel<false, kU, kG>), grid, dim3(256), 0, s, p, items, px);
+    };
+    auto go_g = [&](auto units_c) {
+      if (G == 1) go(units_c, std::integral_constant<int, 1>());
+      else if (G == 2) go(units_c, std::integral_constant<int, 2>());
+      else if (G == 4) go(units_c, std::integral_constant<int, 4>());
+      else go(units_c, std::integral_constant<int, 8>());
+    };
+    if (units) go_g(std::true_type());
+    else go_g(std::false_type());
     return hipGetLastError();
   }
   if (p.unit_table != nullptr) return hipErrorInvalidValue;   // unit rows come as fp16 only
