@@ -175,6 +175,9 @@ void prefill_roles_kernel(PrefillParams p, int n_units) {
   const float c = p.scale_log2 == 0.f ? 0x1p-100f : fabsf(p.scale_log2);
 
   if (is_score) {
+    // the score waves set each step's length (the value waves wait for
+    // them at the barrier): their instructions go first on a shared SIMD
+    __builtin_amdgcn_s_setprio(1);
     // =====================================================================
     // Score waves
     // =====================================================================
