@@ -241,16 +241,19 @@ __global__ __launch_bounds__(256) void rotate_append_kernel(RotateAppendParams p
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int e0 = lane * E;
   float v[E];
-  if (wave < p.q_rows) {
-    load_any<E>(p.q, wave * p.qs + e0, p.q_bf16, p.q_vec, v);
+  // New latent rows first: their page lookup is a chain of dependent loads,
+  // which then overlaps the query rows instead of ending the launch.
+  if (wave >= p.n_rows) {
+    const int64_t qr = wave - p.n_rows;
+    if (qr >= p.q_rows) return;
+    load_any<E>(p.q, qr * p.qs + e0, p.q_bf16, p.q_vec, v);
     fwht_row<E>(v, lane, 64);
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] *= norm;
-    store_any<E>(p.q_out, wave * p.qos + e0, p.q_out_bf16, p.q_vec, v);
+    store_any<E>(p.q_out, qr * p.qos + e0, p.q_out_bf16, p.q_vec, v);
     return;
   }
-  const int64_t t = wave - p.q_rows;
-  if (t >= p.n_rows) return;
+  const int64_t t = wave;
   // The row's page is looked up before the transform, so those dependent
   // loads overlap the row load and the butterflies.  Without caches the
   // row tables and the paging sizes are not given (they may be NULL / 0).
