@@ -59,6 +59,7 @@ typedef __attribute__((address_space(4))) const int32_t const_i32_t;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int scalar_load(const int32_t* p) { return *(const const_i32_t*)p; }
 
@@ -653,8 +654,10 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
         }
         const int cb = 8 * lq + 4 * mm + q;     // 8-column block of columns 64lq + 32mm + 8q ..
-        *reinterpret_cast<uint2*>(part_h + (static_cast<int64_t>(cb) * p.heads + head) * 8 + 4 * half) =
-            make_uint2(w[0], w[1]);
+        // streaming stores: read once, by the merge, from memory
+        const u32x2_t wv = {w[0], w[1]};
+        __builtin_nontemporal_store(
+            wv, reinterpret_cast<u32x2_t*>(part_h + (static_cast<int64_t>(cb) * p.heads + head) * 8 + 4 * half));
       }
   }
   barrier();                                      // B_l: row sums in lsum

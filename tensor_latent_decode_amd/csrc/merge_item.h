@@ -17,6 +17,8 @@
 
 namespace tpla {
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 struct MergePart {
   float m, tot;        // running max and sum of exp(lse_s - m)
   float acc[8];        // sum of exp(lse_s - m) * o_s, 8 columns
@@ -49,7 +51,10 @@ __device__ inline MergePart merge16_partial(const MergeParams& p, int b, int h, 
         const int64_t unit = ut.x + s;
         l[u] = p.ws_lse[unit * p.heads + h];
         f[u] = wsc[(unit * nblk + col / p.blk_cols) * p.heads + h];
-        v[u] = *reinterpret_cast<const uint4*>(wh + ((unit * o8 + cb) * p.heads + h) * 8);
+        // streaming load: each split output is read once
+        const u32x4_t x = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(wh + ((unit * o8 + cb) * p.heads + h) * 8));
+        v[u] = make_uint4(x[0], x[1], x[2], x[3]);
       } else {
         const int64_t row = static_cast<int64_t>(s) * p.batch * p.heads + static_cast<int64_t>(b) * p.heads + h;
         l[u] = p.ws_lse[row];
