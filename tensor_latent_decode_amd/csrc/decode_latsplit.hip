@@ -584,7 +584,10 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   // Split outputs leave as fp16 with one float scale per (row, wave block
   // of 32*MPW columns): o = scale * h, |h| <= 1.  That halves the partial
   // traffic of the split merge at a rounding error below 2^-11 of the
-  // block's largest value.
+  // block's largest value.  Split u = split * batch + b holds [DS / 8][heads]
+  // [8] halves (one store instruction writes 8-byte halves of 16-byte
+  // pieces of 32 consecutive heads: 512 contiguous bytes) and scales
+  // [DS / (32*MPW)][heads].
   uint16_t* wh = reinterpret_cast<uint16_t*>(p.ws_o);
   float* wsc = reinterpret_cast<float*>(reinterpret_cast<char*>(p.ws_o) +
                                         fp16_partials_scale_offset(p.num_splits, p.batch, p.heads, DS));
@@ -598,8 +601,9 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
       for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(oacc[mm][ht][r]));
     amax = both_halves_max(amax);
     const float hs = amax > 0.f ? 1.0f / amax : 0.f;
-    const int64_t row = row0 + head0 + ht * 32 + l31;
-    uint16_t* dst = wh + row * DS + 32 * MPW * wave + 4 * half;
+    const int hh = head0 + ht * 32 + l31;
+    const int64_t u = row0 / p.heads;           // split * batch + b
+    uint16_t* dst = wh + (u * (DS / 8) + 4 * MPW * wave) * p.heads * 8 + static_cast<int64_t>(hh) * 8 + 4 * half;
 #pragma unroll
     for (int mm = 0; mm < MPW; ++mm)
 #pragma unroll
@@ -612,9 +616,9 @@ void decode_latsplit_kernel(DecodeParams p, int n_units, int units_per_xcd) {
           w[k] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
         }
-        *reinterpret_cast<uint2*>(dst + mm * 32 + 8 * q) = make_uint2(w[0], w[1]);
+        *reinterpret_cast<uint2*>(dst + static_cast<int64_t>(4 * mm + q) * p.heads * 8) = make_uint2(w[0], w[1]);
       }
-    if (half == 0) wsc[row * NW + wave] = amax * inv_l;
+    if (half == 0) wsc[(u * NW + wave) * p.heads + hh] = amax * inv_l;
   }
 }
 

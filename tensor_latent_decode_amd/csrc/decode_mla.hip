@@ -411,6 +411,7 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd, int hv) {
                                         fp16_partials_scale_offset(p.num_splits, p.batch, p.heads, kDS));
   const float l_tot = both_halves_sum(l_part);
   const int64_t row = row0 + hd;
+  const int64_t su = row0 / p.heads;              // split * batch + b
   if (kh == 0 && half == 0 && real) p.ws_lse[row] = (m_run + __log2f(l_tot)) * kLn2;
   const float inv_l = 1.0f / l_tot;
 #pragma unroll
@@ -424,7 +425,10 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd, int hv) {
     const float hs = amax > 0.f ? 1.0f / amax : 0.f;
 #pragma unroll
     for (int m = 2 * blk; m < 2 * blk + 2; ++m) {
-      uint16_t* dst = wh + row * kDS + 32 * (MTW * kh + m) + 4 * half;
+      // split u holds [kDS / 8][heads][8] halves: one store instruction
+      // writes 16-byte pieces of 32 consecutive heads
+      uint16_t* dst = wh + (su * (kDS / 8) + 4 * (MTW * kh + m)) * p.heads * 8 + static_cast<int64_t>(hd) * 8 +
+                      4 * half;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint32_t w[2];
@@ -435,10 +439,10 @@ void decode_mla_kernel(DecodeParams p, int n_units, int units_per_xcd, int hv) {
           w[k] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
         }
-        if (real) *reinterpret_cast<uint2*>(dst + 8 * q) = make_uint2(w[0], w[1]);
+        if (real) *reinterpret_cast<uint2*>(dst + static_cast<int64_t>(q) * p.heads * 8) = make_uint2(w[0], w[1]);
       }
     }
-    if (half == 0 && real) wsc[row * (kDS / 64) + (MTW / 2) * kh + blk] = amax * inv_l;
+    if (half == 0 && real) wsc[(su * (kDS / 64) + (MTW / 2) * kh + blk) * p.heads + hd] = amax * inv_l;
   }
 }
 

@@ -5,8 +5,8 @@
 // lse_s = log sum exp(scores).  The split results combine exactly:
 //     LSE = log sum_s exp(lse_s),   o = sum_s exp(lse_s - LSE) * o_s.
 // Splits without tokens carry lse_s = -inf and get weight 0.  o_s comes as
-// float32, or as fp16 h_s with a float scale per block of columns
-// (o_s = scale * h_s).
+// float32 (generic kernels), or as fp16 h_s with a float scale per block of
+// columns (o_s = scale * h_s; the streaming kernels).
 //
 // Combine: shard g owns latent columns g*d_s .. (g+1)*d_s, so summing the
 // zero-padded shard outputs (the all-reduce of the TPLA abstract) places
@@ -19,29 +19,13 @@
 namespace tpla {
 namespace {
 
-// Four consecutive columns of split s's output for row bh (float32 or
-// scaled fp16 partials).
-template <bool kFp16Parts>
+// Four consecutive columns of split s's float32 output for row bh.
 __device__ __forceinline__ float4 load_part(const MergeParams& p, int s, int64_t bh, int col, int ncol,
                                             bool vec, int64_t stride_s) {
-  if constexpr (kFp16Parts) {
-    const int64_t row = s * stride_s + bh;
-    const uint16_t* h = reinterpret_cast<const uint16_t*>(p.ws_o) + row * p.d_s + col;
-    const float* sc = reinterpret_cast<const float*>(
-        reinterpret_cast<const char*>(p.ws_o) +
-        fp16_partials_scale_offset(p.splits, p.batch, p.heads, p.d_s));
-    const float f = sc[row * (p.d_s / p.blk_cols) + col / p.blk_cols];
-    const uint2 w = *reinterpret_cast<const uint2*>(h);
-    return make_float4(f * static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w.x))),
-                       f * static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w.x >> 16))),
-                       f * static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w.y))),
-                       f * static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w.y >> 16))));
-  } else {
-    const float* src = p.ws_o + (s * stride_s + bh) * p.d_s + col;
-    if (vec) return *reinterpret_cast<const float4*>(src);
-    return make_float4(src[0], ncol > 1 ? src[1] : 0.f, ncol > 2 ? src[2] : 0.f,
-                       ncol > 3 ? src[3] : 0.f);
-  }
+  const float* src = p.ws_o + (s * stride_s + bh) * p.d_s + col;
+  if (vec) return *reinterpret_cast<const float4*>(src);
+  return make_float4(src[0], ncol > 1 ? src[1] : 0.f, ncol > 2 ? src[2] : 0.f,
+                     ncol > 3 ? src[3] : 0.f);
 }
 
 // One thread per (b, h, 4 consecutive columns); a wavefront covers 256
@@ -52,7 +36,7 @@ __device__ __forceinline__ float4 load_part(const MergeParams& p, int s, int64_t
 // never trusted).  Workgroup n handles items ((n % 8) * per_xcd + n / 8) *
 // 256 ..., i.e. sequences are spread over the XCDs in the same order as the
 // split-K kernel placed them.
-template <bool kBf16Out, bool kFp16Parts>
+template <bool kBf16Out>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_items, int per_xcd) {
   const int n = blockIdx.x;
   const int64_t wg = static_cast<int64_t>(n & 7) * per_xcd + (n >> 3);
@@ -80,7 +64,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_ite
     for (int u = 0; u < kC; ++u) {
       const int s = min(s0 + u, p.splits - 1);
       l[u] = lse_in[s * stride_s];
-      v[u] = load_part<kFp16Parts>(p, s, bh, col, ncol, vec, stride_s);
+      v[u] = load_part(p, s, bh, col, ncol, vec, stride_s);
     }
     float cm = m;
 #pragma unroll
@@ -130,14 +114,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_ite
 // fp16 split outputs (streaming kernels; d_s a multiple of blk_cols, which
 // is a multiple of 8): one thread per (b, h, 8 consecutive columns) with
 // 16-byte partial loads, up to 16 splits per memory round trip, as above.
-// Two layouts:
-//   rows (s, b, h) for s < splits, each [d_s] with scales [d_s / blk_cols]:
-//     threads take the columns of a row fastest (a wavefront reads two whole
-//     256-column rows of a split);
-//   kUnits: sequence b owns units first_b .. first_b + n_b - 1 (unit
-//     table); unit u holds [d_s / 8][heads][8] halves and scales
-//     [d_s / blk_cols][heads]: threads take the heads fastest, so a
-//     wavefront reads 1 KB of one unit at a time.
+// The split outputs of (split or unit) u hold [d_s / 8][heads][8] halves
+// and scales [d_s / blk_cols][heads]; u = s * batch + b for uniform splits,
+// or, with a unit table, sequence b owns units first_b .. first_b + n_b - 1.
+// A wavefront takes 8 heads x 8 column blocks of one sequence, so it reads
+// 128-byte runs (8 heads of one block) and writes runs of 8 blocks of one
+// head.
 template <bool kBf16Out, bool kUnits, int G>
 __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_items, int per_xcd) {
   const int n = blockIdx.x;
@@ -147,25 +129,13 @@ __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_i
   const int g = static_cast<int>(tid % G);
   if (item >= n_items) return;                  // whole groups leave together
   const int o8 = p.d_s / 8;
-  int b, h, cb;
-  if constexpr (kUnits) {
-    // a wavefront takes 8 heads x 8 column blocks: reads in 128-byte runs
-    // (8 heads of one block), writes in runs of 8 blocks of one head
-    const int64_t per_seq = static_cast<int64_t>(o8) * p.heads;
-    b = static_cast<int>(item / per_seq);
-    const int r = static_cast<int>(item % per_seq);
-    const int rest = r >> 6;
-    h = (rest % (p.heads / 8)) * 8 + (r & 7);
-    cb = (rest / (p.heads / 8)) * 8 + ((r >> 3) & 7);
-    // per_seq is a multiple of 64 (heads % 8 == 0, d_s / 8 % 8 == 0): one
-    // sequence per wavefront, whose unit range comes by a scalar load
-    b = __builtin_amdgcn_readfirstlane(b);
-  } else {
-    const int64_t bh = item / o8;
-    cb = static_cast<int>(item % o8);
-    b = static_cast<int>(bh / p.heads);
-    h = static_cast<int>(bh % p.heads);
-  }
+  const int64_t per_seq = static_cast<int64_t>(o8) * p.heads;   // a multiple of 64
+  // one sequence per wavefront, whose unit range comes by a scalar load
+  const int b = __builtin_amdgcn_readfirstlane(static_cast<int>(item / per_seq));
+  const int ri = static_cast<int>(item % per_seq);
+  const int rest = ri >> 6;
+  const int h = (rest % (p.heads / 8)) * 8 + (ri & 7);
+  const int cb = (rest / (p.heads / 8)) * 8 + ((ri >> 3) & 7);
   int2 ut = make_int2(0, p.splits);
   if constexpr (kUnits) {
     typedef __attribute__((address_space(4))) const int32_t const_i32_t;
@@ -214,16 +184,17 @@ hipError_t launch_c(const PartPtrs& parts, int tp, int batch, int heads, int d_s
 
 }  // namespace
 
-template <bool kBf16Out, bool kFp16Parts>
+template <bool kBf16Out>
 void launch_m(const MergeParams& p, int64_t n_items, int64_t per_xcd, hipStream_t s) {
-  hipLaunchKernelGGL((merge_kernel<kBf16Out, kFp16Parts>), dim3(static_cast<unsigned>(8 * per_xcd)),
+  hipLaunchKernelGGL((merge_kernel<kBf16Out>), dim3(static_cast<unsigned>(8 * per_xcd)),
                      dim3(256), 0, s, p, n_items, static_cast<int>(per_xcd));
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
-  // unit rows: waves of 8 heads x 8 column blocks
-  if (p.unit_table != nullptr && (p.heads % 8 != 0 || (p.d_s / 8) % 8 != 0)) return hipErrorInvalidValue;
-  if (p.blk_cols != 0 && p.blk_cols % 8 == 0 && p.d_s % p.blk_cols == 0) {
+  // fp16 split outputs: waves of 8 heads x 8 column blocks of one sequence
+  if (p.blk_cols != 0) {
+    if (p.blk_cols % 8 != 0 || p.d_s % p.blk_cols != 0 || p.heads % 8 != 0 || (p.d_s / 8) % 8 != 0)
+      return hipErrorInvalidValue;
     const int64_t items = static_cast<int64_t>(p.batch) * p.heads * (p.d_s / 8);
     const bool units = p.unit_table != nullptr;
     // lanes per item: past 16 splits (two memory round trips for one lane)
@@ -255,20 +226,13 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
     else go_g(std::false_type());
     return hipGetLastError();
   }
-  if (p.unit_table != nullptr) return hipErrorInvalidValue;   // unit rows come as fp16 only
+  if (p.unit_table != nullptr) return hipErrorInvalidValue;   // units come as fp16 only
   const int64_t n_items = static_cast<int64_t>(p.batch) * p.heads * ((p.d_s + 3) / 4);
   const int64_t wgs = (n_items + 255) / 256;
   const int64_t per_xcd = (wgs + 7) / 8;
   if (8 * per_xcd > 0x7FFFFFFF) return hipErrorInvalidValue;
-  // fp16 partials: 4-column groups never straddle a scale block
-  if (p.blk_cols != 0 && (p.blk_cols % 4 != 0 || p.d_s % p.blk_cols != 0)) return hipErrorInvalidValue;
-  if (p.blk_cols != 0) {
-    if (p.out_bf16) launch_m<true, true>(p, n_items, per_xcd, s);
-    else launch_m<false, true>(p, n_items, per_xcd, s);
-  } else {
-    if (p.out_bf16) launch_m<true, false>(p, n_items, per_xcd, s);
-    else launch_m<false, false>(p, n_items, per_xcd, s);
-  }
+  if (p.out_bf16) launch_m<true>(p, n_items, per_xcd, s);
+  else launch_m<false>(p, n_items, per_xcd, s);
   return hipGetLastError();
 }
 

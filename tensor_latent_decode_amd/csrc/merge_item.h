@@ -5,12 +5,10 @@
 // memory round trip (every load of a chunk is issued before any is used),
 // with a running max across chunks.  The splits of an item may be shared by
 // G adjacent lanes (lane g takes splits g, g + G, ...), whose partial
-// results then combine exactly the same way across the lanes.  Two layouts
-// of the split outputs:
-//   rows (s, b, h) for s < splits, each [d_s] with scales [d_s / blk_cols];
-//   kUnits: sequence b owns units ut.x .. ut.x + ut.y - 1; unit u holds
-//     [d_s / 8][heads][8] halves and scales [d_s / blk_cols][heads], lse
-//     [heads].
+// results then combine exactly the same way across the lanes.  Split (or
+// unit) u holds [d_s / 8][heads][8] halves, scales [d_s / blk_cols][heads]
+// and lse [heads]: u = s * batch + b for uniform splits; kUnits: sequence b
+// owns units ut.x .. ut.x + ut.y - 1.
 #pragma once
 
 #include "tpla_internal.h"
@@ -34,7 +32,7 @@ __device__ inline MergePart merge16_partial(const MergeParams& p, int b, int h, 
   const uint16_t* wh = reinterpret_cast<const uint16_t*>(p.ws_o);
   const float* wsc = reinterpret_cast<const float*>(
       reinterpret_cast<const char*>(p.ws_o) +
-      fp16_partials_scale_offset(p.splits, kUnits ? 1 : p.batch, p.heads, p.d_s));
+      fp16_partials_scale_offset(p.splits, kUnits ? 1 : p.batch, p.heads, p.d_s));   // after every row
   constexpr int kC = 16;
   MergePart r;
 #pragma unroll
@@ -47,19 +45,17 @@ __device__ inline MergePart merge16_partial(const MergeParams& p, int b, int h, 
 #pragma unroll
     for (int u = 0; u < kC; ++u) {
       const int s = min(s0 + u * G, nsplit - 1);
+      const int64_t unit = kUnits ? static_cast<int64_t>(ut.x) + s : static_cast<int64_t>(s) * p.batch + b;
+      l[u] = p.ws_lse[unit * p.heads + h];
+      f[u] = wsc[(unit * nblk + col / p.blk_cols) * p.heads + h];
       if constexpr (kUnits) {
-        const int64_t unit = ut.x + s;
-        l[u] = p.ws_lse[unit * p.heads + h];
-        f[u] = wsc[(unit * nblk + col / p.blk_cols) * p.heads + h];
-        // streaming load: each split output is read once
+        // streaming load: each unit output is read once (written as 512-byte
+        // runs by streaming stores)
         const u32x4_t x = __builtin_nontemporal_load(
             reinterpret_cast<const u32x4_t*>(wh + ((unit * o8 + cb) * p.heads + h) * 8));
         v[u] = make_uint4(x[0], x[1], x[2], x[3]);
       } else {
-        const int64_t row = static_cast<int64_t>(s) * p.batch * p.heads + static_cast<int64_t>(b) * p.heads + h;
-        l[u] = p.ws_lse[row];
-        f[u] = wsc[row * nblk + col / p.blk_cols];
-        v[u] = *reinterpret_cast<const uint4*>(wh + row * p.d_s + col);
+        v[u] = *reinterpret_cast<const uint4*>(wh + ((unit * o8 + cb) * p.heads + h) * 8);
       }
     }
     float cm = r.m;
