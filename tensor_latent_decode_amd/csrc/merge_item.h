@@ -32,7 +32,7 @@ __device__ inline MergePart merge16_partial(const MergeParams& p, int b, int h, 
   const uint16_t* wh = reinterpret_cast<const uint16_t*>(p.ws_o);
   const float* wsc = reinterpret_cast<const float*>(
       reinterpret_cast<const char*>(p.ws_o) +
-      fp16_partials_scale_offset(p.splits, kUnits ? 1 : p.batch, p.heads, p.d_s));   // after every row
+      fp16_partials_scale_offset(p.splits, kUnits ? 1 : p.batch, p.heads, p.d_s));   // scales follow the rows
   constexpr int kC = 16;
   MergePart r;
 #pragma unroll
@@ -55,6 +55,7 @@ __device__ inline MergePart merge16_partial(const MergeParams& p, int b, int h, 
             reinterpret_cast<const u32x4_t*>(wh + ((unit * o8 + cb) * p.heads + h) * 8));
         v[u] = make_uint4(x[0], x[1], x[2], x[3]);
       } else {
+        // split rows of the 64-head and MLA kernels (plain stores)
         v[u] = *reinterpret_cast<const uint4*>(wh + ((unit * o8 + cb) * p.heads + h) * 8);
       }
     }
