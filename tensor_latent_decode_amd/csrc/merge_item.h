@@ -42,12 +42,38 @@ __device__ inline MergePart merge16_partial(const MergeParams& p, int b, int h, 
   for (int s0 = g; s0 < nsplit; s0 += kC * G) {
     float l[kC], f[kC];
     uint4 v[kC];
+    // One lane per item (G == 1): the wavefront's 8 column blocks of 8 heads
+    // share each head's lse and scale, so lane r loads those of splits r/8
+    // and r/8 + 8 for its head (lanes r and r % 8 + 8k hold the same head)
+    // and the others come by shuffle: 4 loads instead of 32.
+    const bool shared = G == 1 && p.blk_cols % 64 == 0;
+    if (shared) {
+      const int lane = static_cast<int>(threadIdx.x & 63);
+      float la, lb, fa, fb;
+      {
+        const int sa = min(s0 + (lane >> 3), nsplit - 1), sb = min(s0 + (lane >> 3) + 8, nsplit - 1);
+        const int64_t ua = kUnits ? static_cast<int64_t>(ut.x) + sa : static_cast<int64_t>(sa) * p.batch + b;
+        const int64_t ub = kUnits ? static_cast<int64_t>(ut.x) + sb : static_cast<int64_t>(sb) * p.batch + b;
+        la = p.ws_lse[ua * p.heads + h];
+        lb = p.ws_lse[ub * p.heads + h];
+        fa = wsc[(ua * nblk + col / p.blk_cols) * p.heads + h];
+        fb = wsc[(ub * nblk + col / p.blk_cols) * p.heads + h];
+      }
+#pragma unroll
+      for (int u = 0; u < kC; ++u) {
+        const int src = ((u & 7) << 3) | (lane & 7);
+        l[u] = __shfl(u < 8 ? la : lb, src);
+        f[u] = __shfl(u < 8 ? fa : fb, src);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < kC; ++u) {
       const int s = min(s0 + u * G, nsplit - 1);
       const int64_t unit = kUnits ? static_cast<int64_t>(ut.x) + s : static_cast<int64_t>(s) * p.batch + b;
-      l[u] = p.ws_lse[unit * p.heads + h];
-      f[u] = wsc[(unit * nblk + col / p.blk_cols) * p.heads + h];
+      if (!shared) {
+        l[u] = p.ws_lse[unit * p.heads + h];
+        f[u] = wsc[(unit * nblk + col / p.blk_cols) * p.heads + h];
+      }
       if constexpr (kUnits) {
         // streaming load: each unit output is read once (written as 512-byte
         // runs by streaming stores)
