@@ -671,7 +671,7 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
 // Tuning of the launch below (kept as named constants so the choice is
 // visible in one place).
 constexpr bool kRolesCopyS = false;
-constexpr int kRolesKPre = 4, kRolesPPre = 3, kRolesPrioS = 0, kRolesPrioV = 0;
+constexpr int kRolesKPre = 4, kRolesPPre = 3, kRolesPrioS = 1, kRolesPrioV = 0;
 constexpr int kRolesPro = 2;
 
 }  // namespace
