@@ -290,12 +290,13 @@ tpla_status tpla_decode_workspace_size(const tpla_decode_args* args, size_t* byt
  * same lengths the device array holds).  The automatic split count sees
  * only max_seq_len, which for a ragged batch leaves many splits empty and a
  * few long ones; this one models a launch of the streaming kernel (work
- * units in launch order, their XCD, one or two workgroups per CU, a fixed
+ * units in launch order, their XCD, one workgroup per CU, a fixed
  * start and finish per unit) and returns the count with the shortest
  * modelled launch, preferring fewer splits on ties.  For shapes that do not
  * run the streaming kernel it returns the automatic count, and for the
- * 128-head d_s = 256 kernel, whose automatic plan balances units over the
- * device's lengths itself, it returns 0 (automatic).  It reads
+ * 128-head d_s = 256 and 64-head d_s = 128 kernels, whose automatic plan
+ * balances units over the device's lengths itself, it returns 0
+ * (automatic).  It reads
  * nothing on the device and launches nothing; args->num_splits is ignored.
  * Errors: as tpla_decode_workspace_size; TPLA_ERR_NULL for a NULL
  * seq_lens_host or num_splits.
@@ -330,10 +331,11 @@ tpla_status tpla_decode_suggest_splits_cus(const tpla_decode_args* args,
  *
  * The work is split over tokens; each split keeps a running max and sum
  * (online softmax) and the splits are merged by log-sum-exp before `out` is
- * written.  On the 128-head d_s = 256 kernel the splits are work units
- * derived on the device from seq_lens: with num_splits = 0, sequence b's
- * ceil(L_b / 64) tiles are cut into units of c tiles, c the smallest chunk
- * that leaves at most one unit per CU (capped at 1024 tiles), so a ragged
+ * written.  On the d_s = 256 (heads % 128 == 0) and d_s = 128 (heads % 64
+ * == 0) kernel the splits are work units derived on the device from
+ * seq_lens: with num_splits = 0, sequence b's ceil(L_b / 64) tiles are cut
+ * into units of c tiles, c the smallest chunk that leaves at most one unit
+ * per CU and head group (capped at 1024 tiles), so a ragged
  * batch gives every CU about the same work; with num_splits > 0 the chunk
  * is the uniform one of that many splits of max_seq_len.
  *

@@ -1,48 +1,58 @@
 // Split-K decode of one TPLA shard on the matrix cores with separate score
-// and value waves (gfx950): 128-head groups, latent slice d_s = 256, rope 64.
+// and value waves (gfx950): 128-head groups with latent slice d_s = 256, or
+// 64-head groups with d_s = 128; rope 64.
 //
 // Per-shard attention of the absorbed query slice plus the whole rope query
 // over the shard's cached rows [latent slice || rope]; the value is the
 // latent slice; the softmax is the shard's own (TPLA abstract; edgentiq
 // blog, "How TPLA Works: Smart Slicing and Reparameterization").
 //
-// One workgroup of eight waves per (work unit, 128 heads), one workgroup
-// per CU, two waves per SIMD.  A work unit is a token range of one sequence
-// from the unit map of the lengths (unit_map.h): about one per CU, equal in
-// tiles whatever the mix of lengths.  The waves take two roles:
+// One workgroup per (work unit, HG heads), one workgroup per CU.  A work
+// unit is a token range of one sequence from the unit map of the lengths
+// (unit_map.h): about one per CU, equal in tiles whatever the mix of
+// lengths.  The waves take two roles:
 //
-//   score waves 0..3   wave h owns heads 32h .. 32h+31:
-//                      S^T[token, head] = K_tile . Q^T over d_s + d_r, then
-//                      P = exp2(c*S - m_ref), stored to LDS as the B
-//                      fragments of the value product (P^T)
-//   value waves 4..7   wave 4+q owns latent columns 64q .. 64q+63 for all
-//                      128 heads: O^T[lat, head] += V^T . P^T
+//   score waves 0..NS-1   wave h owns heads 32h .. 32h+31 (NS = HG / 32):
+//                         S^T[token, head] = K_tile . Q^T over d_s + d_r,
+//                         then P = exp2(c*S - m_ref), stored to LDS as the
+//                         B fragments of the value product (P^T)
+//   value waves NS..NS+3  wave NS+q owns latent columns d_s/4 * q .. for all
+//                         HG heads: O^T[lat, head] += V^T . P^T
 //
-// all on v_mfma_f32_32x32x16_bf16.  A SIMD holds one wave of each role, so
-// the score wave's exponentials and LDS waits overlap the value wave's
-// MFMAs and the other way round; a single wave per SIMD has nothing to run
-// while it waits on LDS.  The query (80 registers) lives only in the score
-// waves and the output accumulators (128 registers) only in the value
-// waves, which is what lets two waves share a SIMD's register file.
+// all on v_mfma_f32_32x32x16_bf16.  Waves w and w+4 share a SIMD, so with
+// 128 heads each SIMD holds one wave of each role: the score wave's
+// exponentials and LDS waits overlap the value wave's MFMAs and the other
+// way round.  The query (KS fragments) lives only in the score waves and
+// the output accumulators only in the value waves, which is what lets two
+// waves share a SIMD's register file.
 //
-// Pipeline (tile t in K buffer t % 3, its P^T in ptile[t % 2]); one barrier
-// per step.  Step i:
+// Pipeline (tile t in K buffer t % NB, its P^T in ptile[t % 2]); one
+// barrier per step.  Step i:
 //   score waves   scores of tile i+1 (K fragments from LDS), exponentials,
 //                 P^T of tile i+1 -> ptile[(i+1) % 2]
-//   value waves   copy of tile i+3 -> K buffer i % 3 (global -> LDS DMA),
+//   value waves   copy of tile i+NB -> K buffer i % NB (global -> LDS DMA),
 //                 values of tile i (V^T fragments read during step i-1,
 //                 P^T from ptile[i % 2]), V^T fragments of tile i+1 from
-//                 K buffer (i+1) % 3, then wait for tile i+2
-// so every copy has two steps to land and a K buffer is free once the step
-// that scored its tile is over.
+//                 K buffer (i+1) % NB, then wait for tile i+2
+// so every copy has NB - 1 steps to land and NB - 2 tiles are in flight
+// while one is read.  128 heads over 256 columns: 40 KiB tiles, NB = 3;
+// 64 heads over 128 columns: 24 KiB tiles, NB = 5.
 //
-// The rest follows the single-role kernel in decode_latsplit.hip: swizzled
-// tile rows in LDS (no bank conflicts on the K, V^T and P^T reads), V^T
-// fragments from transposing LDS reads in the token order of the P^T
-// fragments, a fixed softmax reference (the split's first tile max) with a
-// rerun if a later tile exceeds it by more than 2^64, fp16 split outputs
-// with a float scale per 64 columns, and units spread so that the splits of
-// a sequence share an XCD.
+// * Tile rows in LDS: 16-byte chunk c of row r sits at (c & ~7) |
+//   ((c & 7) ^ swz(r)), which keeps the score A-fragment reads (16 rows, one
+//   chunk, per 16 lanes), the transposing V^T reads and the P^T reads free
+//   of bank conflicts.
+// * V^T fragments come straight from the K tile by transposing LDS reads
+//   (ds_read_b64_tr_b16): in each group of 16 lanes, lane j receives
+//   element j % 4 of the 8 bytes read by lanes 4k + j / 4, so lane 4k + q
+//   reading token row t_k, columns 4q .. 4q+3 hands lane j four tokens of
+//   column j, half of a value A fragment.  The tokens are taken in the order
+//   of the P^T fragments (16j + 8*(e/4) + 4h + e%4 for element e of fragment
+//   j in lane half h), so no other reordering is needed.
+// * Softmax against a fixed reference (the unit's first tile max), with a
+//   rerun if a later tile exceeds it by more than 2^64.
+// * Split outputs in fp16 with a float scale per 64 columns.
+// * Units are spread so that the pieces of a sequence share an XCD.
 #include <type_traits>
 
 #include "tpla_internal.h"
@@ -152,10 +162,12 @@ struct CopyJob {
   uint32_t lds;
 };
 
-template <int DS, int DR, bool kCopyS, int KPRE, int PPRE, int PRIO_S, int PRIO_V, int kPro>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+template <int HG, int DS, int DR, int NB, int KPRE, int PPRE, int PRIO_S, int PRIO_V, int kPro>
+__global__ __attribute__((amdgpu_flat_work_group_size((HG / 32 + 4) * 64, (HG / 32 + 4) * 64),
+                          amdgpu_waves_per_eu(2, 2)))
 void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
-  constexpr int HG = 128;                   // heads per workgroup
+  // HG heads per workgroup; NB K buffers (tile t in buffer t % NB, NB - 2
+  // tiles in flight while one is read and one waits)
   constexpr int NS = HG / 32;               // score waves (one 32-head tile each)
   constexpr int NV = 4;                     // value waves
   constexpr int D = DS + DR;
@@ -165,15 +177,22 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   constexpr int KS = D / 16;                // k-steps of the score product
   constexpr int MPW = DS / 32 / NV;         // 32-column latent tiles per value wave
   constexpr int NPF = NS * 4;               // P^T fragments per tile: (head tile, 16 tokens)
-  constexpr int NB = 3;                     // K buffers
-  static_assert(NS == 4 && NV == 4, "four waves per role");
+  constexpr int HF = NPF / 2;               // ... of tokens 0..31 (the rest: 32..63)
+  static_assert((NS == 4 || NS == 2) && NV == 4, "two or four score waves, four value waves");
+  static_assert(NB == 3 || NB == 5, "K buffers");
   static_assert(SLOTS % (4 * 64) == 0, "tile must split evenly over the copying waves");
   static_assert(CPR % 8 == 0 && DS % 64 == 0 && DR % 16 == 0, "shape");
-  static_assert(MPW == 2, "value waves own two latent tiles");
-  static_assert(IPT <= NPF && IPT <= 2 * KS && 3 * IPT < 64, "copies per step");
+  static_assert(MPW == 1 || MPW == 2, "value waves own one or two latent tiles");
+  static_assert(IPT <= NPF && IPT <= 2 * KS && (NB - 1) * IPT < 64, "copies per step");
   static_assert(kMaxTiles % (NS * 64) == 0, "tile table fill");
-  static_assert(KPRE >= 2 && KPRE <= 12 && PPRE >= 2 && PPRE <= 8, "prefetch depths");
-  static_assert(kPro >= 1 && kPro <= 3, "tiles copied before the first barrier");
+  static_assert(KPRE >= 2 && KPRE <= 12 && PPRE >= 2 && PPRE <= HF, "prefetch depths");
+  static_assert(kPro >= 1 && kPro <= NB, "tiles copied before the first barrier");
+  // The 16 exponentials of one 32-token tile ride on one score chain of KS
+  // k-steps: k-step kk takes exponentials exp_lo(kk) .. exp_lo(kk + 1) - 1.
+  // The P^T fragments of tokens 32..63 of the previous tile are complete
+  // after step kSignal of the tile's MFMA stream.
+  auto exp_lo = [](int kk) constexpr { return KS >= 16 ? (kk < 16 ? kk : 16) : (kk * 16) / KS; };
+  constexpr int kSignal = KS > 16 ? 16 : KS;
 
   __shared__ __attribute__((aligned(1024))) uint4 ktile[NB][SLOTS];
   __shared__ __attribute__((aligned(1024))) uint4 ptile[2][NPF * 64];
@@ -181,6 +200,9 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   __shared__ float lsum[HG];
   __shared__ int flags[NS];
   __shared__ int pcount;                 // tiles whose P^T fragments 2, 3 are in LDS (x NS)
+  // with one latent tile per value wave, two waves share a 64-column scale
+  // block: their block maxima meet here
+  __shared__ float vmax[MPW == 1 ? NV : 1][MPW == 1 ? HG : 1];
 
   // ---- work unit ----
   // Launch slot n -> unit u (XCD-aware: consecutive units, the head groups
@@ -308,8 +330,6 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
       const int t = k * NS * 64 + static_cast<int>(threadIdx.x);
       if (t < ntiles) trow[t] = tile_row(t, fpg[k]);
     }
-    uint32_t src_off[IPT];
-    if constexpr (kCopyS) copy_offsets(ht, src_off);
 
     // Score A fragment (token rows 32*mt + l31, k-step kk) of the tile at T.
     int qk_off[4];
@@ -359,12 +379,10 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     // tile under chain 0 (then its P^T fragments 2, 3 are signalled), token
     // tile 0 of this tile under chain 1; this tile's token tile 1 stays
     // pending in sp.  The first tile of a pass sets the reference max
-    // first.  cj: this wave's copy of the step (spread over the chains).
-    auto score_tile = [&](int t, const CopyJob& cj, auto first_c, auto masked_c, auto copy_c,
-                          auto careful_c) {
+    // first.
+    auto score_tile = [&](int t, auto first_c, auto masked_c, auto careful_c) {
       constexpr bool first = decltype(first_c)::value;
       constexpr bool masked = decltype(masked_c)::value;
-      constexpr bool do_copy = decltype(copy_c)::value;
       const char* T = reinterpret_cast<const char*>(&ktile[t % NB][0]);
       uint4* pcur = &ptile[t & 1][0];
       uint4* pprev = &ptile[(t + 1) & 1][0];
@@ -383,13 +401,14 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
         const int mt = n2 / KS, kk = n2 % KS;
         sc[mt] = mfma(ka[n2 % KPRE], qf[kk], sc[mt]);
         if (n2 + KPRE < 2 * KS) ka[n2 % KPRE] = rd_k(T, (n2 + KPRE) % KS, (n2 + KPRE) / KS);
-        if (!first && mt == 0 && kk < 16) expo(sp[kk], 16 + kk, pprev, 0, kFalse, careful_c);
-        if (!first && mt == 0 && kk == 16) signal();
-        if (!first && mt == 1 && kk < 16) expo(sc[0][kk], kk, pcur, lim, masked_c, careful_c);
-        if (do_copy) {
+        if (!first && mt == 0) {
 #pragma unroll
-          for (int ci = 0; ci < IPT; ++ci)
-            if ((ci * 2 * KS) / IPT == n2) copy_chunk(cj, src_off, ht, ci);
+          for (int e = exp_lo(kk); e < exp_lo(kk + 1); ++e) expo(sp[e], 16 + e, pprev, 0, kFalse, careful_c);
+        }
+        if (!first && n2 == kSignal) signal();
+        if (!first && mt == 1) {
+#pragma unroll
+          for (int e = exp_lo(kk); e < exp_lo(kk + 1); ++e) expo(sc[0][e], e, pcur, lim, masked_c, careful_c);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -409,22 +428,15 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
       }
       sp = sc[1];
     };
-    // Step t-1: score tile t (after barrier B_{t-1}); with kCopyS also copy
-    // tile t+2 into K buffer (t+2) % 3 and wait for tile t+1.
+    // Step t-1: score tile t (after barrier B_{t-1}).
     auto sstep = [&](int t, auto masked_c, auto careful_c) {
-      CopyJob cj = none;
-      if constexpr (kCopyS) {
-        const uint32_t row64 = __builtin_amdgcn_readfirstlane(trow[min(t + 2, ntiles - 1)]);
-        cj = make_job(t + 2, (t + 2) % NB, row64, ntiles, t1);
-      }
       barrier();                                  // B_{t-1}
-      score_tile(t, cj, kFalse, masked_c, std::integral_constant<bool, kCopyS>(), careful_c);
-      if constexpr (kCopyS) wait_vm<IPT>();       // tile t+1
+      score_tile(t, kFalse, masked_c, careful_c);
     };
     // One pass over the split's tiles.
     auto pass = [&](auto careful_c) {
-      if (nfull == 0) score_tile(0, none, kTrue, kTrue, kFalse, careful_c);
-      else score_tile(0, none, kTrue, kFalse, kFalse, careful_c);
+      if (nfull == 0) score_tile(0, kTrue, kTrue, careful_c);
+      else score_tile(0, kTrue, kFalse, careful_c);
       // steps: tile t = i + 1 is scored after barrier B_i; only the last
       // tile can be partial
       for (int t = 1; t < nfull; ++t) sstep(t, kFalse, careful_c);
@@ -454,7 +466,6 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
       barrier();                                  // B_a: tile 0 in, table written
       if (careful) pass(kTrue);
       else pass(kFalse);
-      if constexpr (kCopyS) wait_vm<0>();         // trailing copies land
       barrier();                                  // B_end
       const float l_tot = both_halves_sum(l_part);
       const bool lane_inf = l_tot == INFINITY;
@@ -488,30 +499,33 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   // =======================================================================
   if constexpr (PRIO_V > 0) __builtin_amdgcn_s_setprio(PRIO_V);
   const int lq = wave - NS;
-  // block ids of tiles 0..2 (scalar loads; index clamped into the table row)
-  int pg[3];
+  // block ids of tiles 0..NB-1 (scalar loads; index clamped into the table row)
+  int pg[NB];
 #pragma unroll
-  for (int t = 0; t < 3; ++t)
+  for (int t = 0; t < NB; ++t)
     pg[t] = scalar_load(bt_row + min((t0 + t * kTile) / bs, p.max_blocks - 1));
-  asm volatile("" : : "s"(pg[0]), "s"(pg[1]), "s"(pg[2]));
+#pragma unroll
+  for (int t = 0; t < NB; ++t) asm volatile("" : : "s"(pg[t]));
   uint32_t src_off[IPT];
   copy_offsets(lq, src_off);
 
-  // Value A fragment (latent tile 2*lq + mm, token k-step j) of the tile at
-  // T: two transposing reads, token rows 16j + 4h + k and 16j + 8 + 4h + k
+  // Value A fragment (latent tile MPW*lq + mm, token k-step j) of the tile
+  // at T: two transposing reads, token rows 16j + 4h + k and 16j + 8 + 4h + k
   // (the swizzle depends on the row's low four bits only, so j moves the
-  // address by whole 16-row strides).
-  uint32_t tr_off[2][2];
+  // address by whole 16-row strides).  Chunk c of a row (8 columns) sits at
+  // (c & ~7) | ((c & 7) ^ swz(row)).
+  uint32_t tr_off[2][MPW];
   {
     const int trk = (lane & 15) >> 2, trq = lane & 3, trg = (lane >> 4) & 1;
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int row = 8 * rr + 4 * half + trk;
 #pragma unroll
-      for (int mo = 0; mo < 2; ++mo)
-        tr_off[rr][mo] = static_cast<uint32_t>(128 * lq + row * CPR * 16 +
-                                               ((4 * mo + 2 * trg + (trq >> 1)) ^ swz(row)) * 16 +
+      for (int mo = 0; mo < MPW; ++mo) {
+        const int cc = 4 * MPW * lq + 4 * mo + 2 * trg + (trq >> 1);
+        tr_off[rr][mo] = static_cast<uint32_t>(row * CPR * 16 + ((cc & ~7) | ((cc & 7) ^ swz(row))) * 16 +
                                                8 * (trq & 1));
+      }
     }
   }
   auto rd_v = [&](const char* T, int mm, int j) -> bf16x8_t {
@@ -520,7 +534,7 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  f32x16_t oacc[MPW][NS];    // O^T tiles: latent tile 2*lq + mm, head tile ht
+  f32x16_t oacc[MPW][NS];    // O^T tiles: latent tile MPW*lq + mm, head tile ht
   bf16x8_t vc[MPW][4];       // V^T fragments of the tile whose values are due
 
   // Value product of the tile whose P^T is in ptile[pb] and V^T in vc.  In
@@ -549,15 +563,15 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
       }
       bf16x8_t pa[PPRE];
 #pragma unroll
-      for (int f = 0; f < PPRE; ++f) pa[f] = frag(8 * hf + f);
+      for (int f = 0; f < PPRE; ++f) pa[f] = frag(HF * hf + f);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int f = 8 * hf; f < 8 * hf + 8; ++f) {
+      for (int f = HF * hf; f < HF * hf + HF; ++f) {
         const int ht = f % NS, j = f / NS;
-        const int fl = f - 8 * hf;
+        const int fl = f - HF * hf;
 #pragma unroll
         for (int mm = 0; mm < MPW; ++mm) oacc[mm][ht] = mfma(vc[mm][j], pa[fl % PPRE], oacc[mm][ht]);
-        if (fl + PPRE < 8) pa[fl % PPRE] = frag(f + PPRE);
+        if (fl + PPRE < HF) pa[fl % PPRE] = frag(f + PPRE);
         if (kStep && ht == NS - 1) {
 #pragma unroll
           for (int mm = 0; mm < MPW; ++mm) vc[mm][j] = rd_v(T, mm, j);
@@ -581,8 +595,8 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[m][ht][r] = 0.f;
     // Tiles 0 .. kPro-1 go out before the first barrier, the rest of the
-    // first three after it: every CU starts at once, and the copies the
-    // memory system holds when tile 0 is wanted delay it.
+    // first NB after it: every CU starts at once, and the copies the memory
+    // system holds when tile 0 is wanted delay it.
     auto copy_tile = [&](int t) {
       const uint32_t row64 = first ? (t < ntiles ? tile_row(t, pg[t]) : 0u)
                                    : __builtin_amdgcn_readfirstlane(trow[min(t, ntiles - 1)]);
@@ -595,25 +609,22 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     wait_vm<(kPro - 1) * IPT>();                  // tile 0
     barrier();                                    // B_a
 #pragma unroll
-    for (int t = kPro; t < 3; ++t) copy_tile(t);
+    for (int t = kPro; t < NB; ++t) copy_tile(t);
     first = false;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) vc[k >> 2][k & 3] = rd_v(reinterpret_cast<const char*>(&ktile[0][0]), k >> 2, k & 3);
-    wait_vm<IPT>();                               // tile 1
+    for (int k = 0; k < 4 * MPW; ++k) vc[k >> 2][k & 3] = rd_v(reinterpret_cast<const char*>(&ktile[0][0]), k >> 2, k & 3);
+    wait_vm<(NB - 2) * IPT>();                    // tile 1
     for (int i = 0; i + 1 < ntiles; ++i) {
       // step i: values of tile i, V^T of tile i+1; unless the score waves
-      // copy, also the copy of tile i+3.  The tile table read waits for this
-      // wave's LDS traffic, as the barrier does anyway.
-      CopyJob cj = none;
-      if constexpr (!kCopyS) {
-        const uint32_t row64 = __builtin_amdgcn_readfirstlane(trow[min(i + 3, ntiles - 1)]);
-        cj = make_job(i + 3, i % NB, row64, ntiles, t1);
-      }
+      // copy, also the copy of tile i+NB into the buffer of tile i.  The
+      // tile table read waits for this wave's LDS traffic, as the barrier
+      // does anyway.
+      const uint32_t row64 = __builtin_amdgcn_readfirstlane(trow[min(i + NB, ntiles - 1)]);
+      const CopyJob cj = make_job(i + NB, i % NB, row64, ntiles, t1);
       barrier();                                  // B_i
       const char* T = reinterpret_cast<const char*>(&ktile[(i + 1) % NB][0]);
-      values(i & 1, T, cj, NS * (i + 1), kTrue, std::integral_constant<bool, !kCopyS>());
-      if constexpr (kCopyS) wait_vm<0>();         // tile 2 (step 0; later steps copy nothing here)
-      else wait_vm<IPT>();                        // tile i+2
+      values(i & 1, T, cj, NS * (i + 1), kTrue, kTrue);
+      wait_vm<(NB - 2) * IPT>();                  // tile i+2
     }
     wait_vm<0>();                                 // trailing copies land
     barrier();                                    // B_end
@@ -628,17 +639,21 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
     barrier();                                    // B_r
   }
   // this wave's columns of the split outputs, from the accumulators: fp16
-  // of o / (block max), then after B_l the block's scale max / l
+  // of o / (block max) and the block's scale max / l, the row sums l from
+  // the score waves after B_l.  A 64-column block is one value wave's
+  // columns (MPW = 2) or two waves' (MPW = 1: their maxima meet in LDS
+  // first).
   float amax_ht[NS];
-#pragma unroll
-  for (int ht = 0; ht < NS; ++ht) {
+  auto block_max = [&](int ht) -> float {
     float amax = 0.f;
 #pragma unroll
     for (int mm = 0; mm < MPW; ++mm)
 #pragma unroll
       for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(oacc[mm][ht][r]));
-    amax = both_halves_max(amax);
-    amax_ht[ht] = amax;
+    return both_halves_max(amax);
+  };
+  auto store_halves = [&](int ht) {
+    const float amax = amax_ht[ht];
     const float hs = amax > 0.f ? 1.0f / amax : 0.f;
     const int head = head0 + ht * 32 + l31;
 #pragma unroll
@@ -653,33 +668,71 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
           w[k] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
         }
-        const int cb = 8 * lq + 4 * mm + q;     // 8-column block of columns 64lq + 32mm + 8q ..
+        // 8-column block of columns 32*MPW*lq + 32mm + 8q ..
+        const int cb = 4 * MPW * lq + 4 * mm + q;
         // streaming stores: read once, by the merge, from memory
         const u32x2_t wv = {w[0], w[1]};
         __builtin_nontemporal_store(
             wv, reinterpret_cast<u32x2_t*>(part_h + (static_cast<int64_t>(cb) * p.heads + head) * 8 + 4 * half));
       }
+  };
+  if constexpr (MPW == 2) {
+#pragma unroll
+    for (int ht = 0; ht < NS; ++ht) {
+      amax_ht[ht] = block_max(ht);
+      store_halves(ht);
+    }
+    barrier();                                    // B_l: row sums in lsum
+  } else {
+#pragma unroll
+    for (int ht = 0; ht < NS; ++ht) {
+      amax_ht[ht] = block_max(ht);
+      if (half == 0) vmax[lq][ht * 32 + l31] = amax_ht[ht];
+    }
+    barrier();                                    // B_l: row sums in lsum, block maxima in vmax
+#pragma unroll
+    for (int ht = 0; ht < NS; ++ht) {
+      amax_ht[ht] = fmaxf(amax_ht[ht], vmax[lq ^ 1][ht * 32 + l31]);
+      store_halves(ht);
+    }
   }
-  barrier();                                      // B_l: row sums in lsum
-  if (half == 0) {
+  if (half == 0 && (MPW == 2 || (lq & 1) == 0)) {
 #pragma unroll
     for (int ht = 0; ht < NS; ++ht)
-      part_sc[lq * p.heads + head0 + ht * 32 + l31] = amax_ht[ht] / lsum[ht * 32 + l31];
+      part_sc[(MPW * lq / 2) * p.heads + head0 + ht * 32 + l31] = amax_ht[ht] / lsum[ht * 32 + l31];
   }
 }
 
-// Tuning of the launch below (kept as named constants so the choice is
+// Tuning of the launches below (kept as named constants so the choice is
 // visible in one place).
-constexpr bool kRolesCopyS = false;
 constexpr int kRolesKPre = 4, kRolesPPre = 3, kRolesPrioS = 1, kRolesPrioV = 0;
 constexpr int kRolesPro = 2;
+
+// HG heads per workgroup with a d_s-wide latent slice and NB K buffers: 128
+// heads over 256 columns (40 KiB tiles, three buffers) or 64 heads over 128
+// columns (24 KiB tiles, five buffers, four tiles in flight).
+template <int HG, int DS, int NB>
+hipError_t launch_roles_t(const DecodeParams& p, hipStream_t s) {
+  const int n_units = p.max_units * (p.heads / HG);
+  const int per_xcd = (n_units + 7) / 8;
+  hipLaunchKernelGGL((decode_roles_kernel<HG, DS, 64, NB, kRolesKPre, kRolesPPre, kRolesPrioS, kRolesPrioV,
+                                         kRolesPro>),
+                     dim3(8 * per_xcd), dim3((HG / 32 + 4) * 64), 0, s, p, n_units, per_xcd);
+  return hipGetLastError();
+}
 
 }  // namespace
 
 int decode_roles_max_tiles() { return kMaxTiles; }
 
 bool decode_roles_supported(int heads, int d_s, int d_r, int block_size) {
-  return heads % 128 == 0 && d_s == 256 && d_r == 64 && block_size % kTile == 0;
+  if (d_r != 64 || block_size % kTile != 0) return false;
+  return (d_s == 256 && heads % 128 == 0) || (d_s == 128 && heads % 64 == 0);
+}
+
+int decode_roles_heads_per_group(int heads, int d_s) {
+  (void)heads;
+  return d_s == 256 ? 128 : 64;
 }
 
 hipError_t launch_decode_roles(const DecodeParams& p, hipStream_t s) {
@@ -687,12 +740,8 @@ hipError_t launch_decode_roles(const DecodeParams& p, hipStream_t s) {
   if (p.chunk > kMaxTiles * kTile || p.chunk % kTile != 0 || p.max_units < 1 ||
       (p.unit_target == 0 && p.chunk < kTile) || p.unit_table == nullptr)
     return hipErrorInvalidValue;
-  const int n_units = p.max_units * (p.heads / 128);
-  const int per_xcd = (n_units + 7) / 8;
-  hipLaunchKernelGGL((decode_roles_kernel<256, 64, kRolesCopyS, kRolesKPre, kRolesPPre, kRolesPrioS,
-                                         kRolesPrioV, kRolesPro>),
-                     dim3(8 * per_xcd), dim3(512), 0, s, p, n_units, per_xcd);
-  return hipGetLastError();
+  if (p.d_s == 256) return launch_roles_t<128, 256, 3>(p, s);
+  return launch_roles_t<64, 128, 5>(p, s);
 }
 
 }  // namespace tpla

@@ -195,7 +195,8 @@ tpla_status plan_decode(const tpla_decode_args* a, Plan* pl, int cus_given = 0) 
     if (a->num_splits == 0) {
       // one unit per CU; more only where a sequence needs more than the
       // largest unit's tiles (or the batch has more sequences than CUs)
-      pl->unit_target = std::max(1, cus / (a->heads / 128));
+      pl->unit_target =
+          std::max(1, cus / (a->heads / tpla::decode_roles_heads_per_group(a->heads, a->d_s)));
       pl->max_units = std::max<int64_t>(
           pl->unit_target, static_cast<int64_t>(a->batch) * ((max_tiles + cap - 1) / cap));
     } else {

@@ -178,6 +178,7 @@ hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_roles(const DecodeParams& p, hipStream_t s);
 bool decode_roles_supported(int heads, int d_s, int d_r, int block_size);
 int decode_roles_max_tiles();      // 64-token tiles one unit of the roles kernel may hold
+int decode_roles_heads_per_group(int heads, int d_s);   // heads of one workgroup (128 or 64)
 bool decode_mla_supported(int heads, int d_s, int d_r, int block_size);
 int decode_mla_max_chunk();
 int decode_mla_group_heads(int heads);   // heads per workgroup of the 512-wide kernel

@@ -250,15 +250,20 @@ def test_suggest_splits_argument_checks():
 
 def test_suggest_splits_for_a_given_cu_count():
     """The cost model without a device: uniform 32K lengths keep the automatic
-    count on the 64-head streaming kernel (16 sequences x 64 heads over 256
-    CUs at two workgroups per CU: 32 splits), the 128-head kernel defers to its
-    own balanced plan (0), and a bad CU count is refused."""
+    count on the 512-wide streaming kernel (16 sequences x one 64-head group
+    over 256 CUs at one workgroup per CU: 16 splits), the 128-head d_s = 256
+    and 64-head d_s = 128 kernels defer to their own balanced plan (0), and a
+    bad CU count is refused."""
     L = tpla.lib()
     lens = np.full(16, 32768, np.int32)
+    mla = _args(batch=16, heads=64, d_s=512, num_blocks=8193, max_blocks_per_seq=512,
+                max_seq_len=32768, q_latent_stride_b=64 * 512, q_rope_stride_b=64 * 64,
+                out_stride_b=64 * 512, out_stride_h=512)
+    assert tpla.decode_suggest_splits(mla, lens, cus=256) == 16
     kimi = _args(batch=16, heads=64, d_s=128, num_blocks=8193, max_blocks_per_seq=512,
                  max_seq_len=32768, q_latent_stride_b=64 * 512, q_rope_stride_b=64 * 64,
                  out_stride_b=64 * 128, out_stride_h=128)
-    assert tpla.decode_suggest_splits(kimi, lens, cus=256) == 32
+    assert tpla.decode_suggest_splits(kimi, lens, cus=256) == 0
     dsv3 = _args(batch=16, num_blocks=8193, max_blocks_per_seq=512, max_seq_len=32768)
     assert tpla.decode_suggest_splits(dsv3, lens, cus=256) == 0
     out = ctypes.c_int32(0)
