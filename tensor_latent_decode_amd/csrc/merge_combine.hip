@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p, int64_t n_ite
 // A wavefront takes 8 heads x 8 column blocks of one sequence, so it reads
 // 128-byte runs (8 heads of one block) and writes runs of 8 blocks of one
 // head.
-template <bool kBf16Out, bool kUnits, int G>
+template <bool kBf16Out, bool kUnits, int G, bool kShared>
 __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_items, int per_xcd) {
   const int n = blockIdx.x;
   const int64_t wg = static_cast<int64_t>(n & 7) * per_xcd + (n >> 3);
@@ -136,13 +136,33 @@ __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_i
   const int rest = ri >> 6;
   const int h = (rest % (p.heads / 8)) * 8 + (ri & 7);
   const int cb = (rest / (p.heads / 8)) * 8 + ((ri >> 3) & 7);
-  int2 ut = make_int2(0, p.splits);
+  MergePart r;
   if constexpr (kUnits) {
-    typedef __attribute__((address_space(4))) const int32_t const_i32_t;
-    const const_i32_t* e = (const const_i32_t*)(p.unit_table + 2 * static_cast<int64_t>(b));
-    ut = make_int2(e[0], e[1]);
+    // The sequence's units come from the unit table.  The merge does not
+    // wait for it: it starts on the uniform map's range (splits / batch
+    // units per sequence, in order; exact for equal lengths), whose loads
+    // share the table's memory round trip, and runs again on the table's
+    // range if that differs.  The entry is a vector load (every lane the
+    // same address), consumed only after the guess's result exists: a
+    // scalar load would be waited for with the kernel arguments.
+    uint64_t ut_addr = reinterpret_cast<uint64_t>(p.unit_table + 2 * static_cast<int64_t>(b));
+    asm volatile("" : "+v"(ut_addr));           // a vector address: the load stays a vector load
+    typedef __attribute__((address_space(1))) const int32_t global_i32_t;
+    const global_i32_t* ut_ptr = reinterpret_cast<const global_i32_t*>(ut_addr);
+    int ux = ut_ptr[0], uy = ut_ptr[1];
+    const int per = p.splits / p.batch;
+    const int2 guess = make_int2(b * per, per);
+    r = merge16_partial<kUnits, kShared>(p, b, h, cb, guess, g, G);
+    // the guess's result and the entry are both in hand here (the compiler
+    // would otherwise compute on the table's range alone, after its load)
+    asm volatile("" : "+v"(r.m), "+v"(r.tot), "+v"(ux), "+v"(uy));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(r.acc[i]));
+    const int2 ut = make_int2(__builtin_amdgcn_readfirstlane(ux), __builtin_amdgcn_readfirstlane(uy));
+    if (ut.x != guess.x || ut.y != guess.y) r = merge16_partial<kUnits, kShared>(p, b, h, cb, ut, g, G);
+  } else {
+    r = merge16_partial<kUnits, kShared>(p, b, h, cb, make_int2(0, p.splits), g, G);
   }
-  MergePart r = merge16_partial<kUnits>(p, b, h, cb, ut, g, G);
   merge_lanes(r, G);
   if (g == 0) merge16_store<kBf16Out>(p, b, h, cb, r);
 }
@@ -213,11 +233,19 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
     auto go = [&](auto units_c, auto g_c) {
       constexpr bool kU = decltype(units_c)::value;
       constexpr int kG = decltype(g_c)::value;
-      if (p.out_bf16) hipLaunchKernelGGL((merge16_kernel<true, kU, kG>), grid, dim3(256), 0, s, p, items, px);
-      else hipLaunchKernelGGL((merge16_kernel<false, kU, kG>), grid, dim3(256), 0, s, p, items, px);
+      if (p.out_bf16) hipLaunchKernelGGL((merge16_kernel<true, kU, kG, false>), grid, dim3(256), 0, s, p, items, px);
+      else hipLaunchKernelGGL((merge16_kernel<false, kU, kG, false>), grid, dim3(256), 0, s, p, items, px);
+    };
+    // one lane per item with 64-column scale blocks: lse and scales shared
+    // by shuffle
+    auto go_shared = [&](auto units_c) {
+      constexpr bool kU = decltype(units_c)::value;
+      if (p.out_bf16) hipLaunchKernelGGL((merge16_kernel<true, kU, 1, true>), grid, dim3(256), 0, s, p, items, px);
+      else hipLaunchKernelGGL((merge16_kernel<false, kU, 1, true>), grid, dim3(256), 0, s, p, items, px);
     };
     auto go_g = [&](auto units_c) {
-      if (G == 1) go(units_c, std::integral_constant<int, 1>());
+      if (G == 1 && p.blk_cols % 64 == 0) go_shared(units_c);
+      else if (G == 1) go(units_c, std::integral_constant<int, 1>());
       else if (G == 2) go(units_c, std::integral_constant<int, 2>());
       else if (G == 4) go(units_c, std::integral_constant<int, 4>());
       else go(units_c, std::integral_constant<int, 8>());

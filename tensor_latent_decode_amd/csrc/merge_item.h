@@ -22,7 +22,10 @@ struct MergePart {
   float acc[8];        // sum of exp(lse_s - m) * o_s, 8 columns
 };
 
-template <bool kUnits>
+// kShared: one lane per item (G == 1) and scale blocks of a multiple of 64
+// columns, so the wavefront's 8 column blocks of 8 heads share each head's
+// lse and scale (see below).
+template <bool kUnits, bool kShared>
 __device__ inline MergePart merge16_partial(const MergeParams& p, int b, int h, int cb, int2 ut, int g,
                                             int G) {
   const int o8 = p.d_s / 8;
@@ -42,35 +45,28 @@ __device__ inline MergePart merge16_partial(const MergeParams& p, int b, int h, 
   for (int s0 = g; s0 < nsplit; s0 += kC * G) {
     float l[kC], f[kC];
     uint4 v[kC];
-    // One lane per item (G == 1): the wavefront's 8 column blocks of 8 heads
-    // share each head's lse and scale, so lane r loads those of splits r/8
-    // and r/8 + 8 for its head (lanes r and r % 8 + 8k hold the same head)
-    // and the others come by shuffle: 4 loads instead of 32.
-    const bool shared = G == 1 && p.blk_cols % 64 == 0;
-    if (shared) {
-      const int lane = static_cast<int>(threadIdx.x & 63);
-      float la, lb, fa, fb;
-      {
-        const int sa = min(s0 + (lane >> 3), nsplit - 1), sb = min(s0 + (lane >> 3) + 8, nsplit - 1);
-        const int64_t ua = kUnits ? static_cast<int64_t>(ut.x) + sa : static_cast<int64_t>(sa) * p.batch + b;
-        const int64_t ub = kUnits ? static_cast<int64_t>(ut.x) + sb : static_cast<int64_t>(sb) * p.batch + b;
-        la = p.ws_lse[ua * p.heads + h];
-        lb = p.ws_lse[ub * p.heads + h];
-        fa = wsc[(ua * nblk + col / p.blk_cols) * p.heads + h];
-        fb = wsc[(ub * nblk + col / p.blk_cols) * p.heads + h];
-      }
-#pragma unroll
-      for (int u = 0; u < kC; ++u) {
-        const int src = ((u & 7) << 3) | (lane & 7);
-        l[u] = __shfl(u < 8 ? la : lb, src);
-        f[u] = __shfl(u < 8 ? fa : fb, src);
-      }
+    // One lane per item (kShared): the wavefront's 8 column blocks of 8
+    // heads share each head's lse and scale, so lane r loads those of splits
+    // r/8 and r/8 + 8 for its head (lanes r and r % 8 + 8k hold the same
+    // head) and the others come by shuffle: 4 loads instead of 32.
+    // Every load of the chunk (lse, scales, split outputs) is issued before
+    // any result is used: one memory round trip.
+    float la = 0.f, lb = 0.f, fa = 0.f, fb = 0.f;
+    const int lane = static_cast<int>(threadIdx.x & 63);
+    if constexpr (kShared) {
+      const int sa = min(s0 + (lane >> 3), nsplit - 1), sb = min(s0 + (lane >> 3) + 8, nsplit - 1);
+      const int64_t ua = kUnits ? static_cast<int64_t>(ut.x) + sa : static_cast<int64_t>(sa) * p.batch + b;
+      const int64_t ub = kUnits ? static_cast<int64_t>(ut.x) + sb : static_cast<int64_t>(sb) * p.batch + b;
+      la = p.ws_lse[ua * p.heads + h];
+      lb = p.ws_lse[ub * p.heads + h];
+      fa = wsc[(ua * nblk + col / p.blk_cols) * p.heads + h];
+      fb = wsc[(ub * nblk + col / p.blk_cols) * p.heads + h];
     }
 #pragma unroll
     for (int u = 0; u < kC; ++u) {
       const int s = min(s0 + u * G, nsplit - 1);
       const int64_t unit = kUnits ? static_cast<int64_t>(ut.x) + s : static_cast<int64_t>(s) * p.batch + b;
-      if (!shared) {
+      if constexpr (!kShared) {
         l[u] = p.ws_lse[unit * p.heads + h];
         f[u] = wsc[(unit * nblk + col / p.blk_cols) * p.heads + h];
       }
@@ -81,8 +77,21 @@ __device__ inline MergePart merge16_partial(const MergeParams& p, int b, int h, 
             reinterpret_cast<const u32x4_t*>(wh + ((unit * o8 + cb) * p.heads + h) * 8));
         v[u] = make_uint4(x[0], x[1], x[2], x[3]);
       } else {
-        // split rows of the 64-head and MLA kernels (plain stores)
+        // split rows of the MLA kernel (plain stores)
         v[u] = *reinterpret_cast<const uint4*>(wh + ((unit * o8 + cb) * p.heads + h) * 8);
+      }
+    }
+    // The results are used only past the test for a chunk without tokens;
+    // marking them used here keeps the compiler from sinking their loads
+    // below it (after the lse round trip).
+#pragma unroll
+    for (int u = 0; u < kC; ++u) asm volatile("" : : "v"(v[u].x), "v"(v[u].y), "v"(v[u].z), "v"(v[u].w));
+    if constexpr (kShared) {
+#pragma unroll
+      for (int u = 0; u < kC; ++u) {
+        const int src = ((u & 7) << 3) | (lane & 7);
+        l[u] = __shfl(u < 8 ? la : lb, src);
+        f[u] = __shfl(u < 8 ? fa : fb, src);
       }
     }
     float cm = r.m;
