@@ -138,28 +138,14 @@ __global__ __launch_bounds__(256) void merge16_kernel(MergeParams p, int64_t n_i
   const int cb = (rest / (p.heads / 8)) * 8 + ((ri >> 3) & 7);
   MergePart r;
   if constexpr (kUnits) {
-    // The sequence's units come from the unit table.  The merge does not
-    // wait for it: it starts on the uniform map's range (splits / batch
-    // units per sequence, in order; exact for equal lengths), whose loads
-    // share the table's memory round trip, and runs again on the table's
-    // range if that differs.  The entry is a vector load (every lane the
-    // same address), consumed only after the guess's result exists: a
-    // scalar load would be waited for with the kernel arguments.
-    uint64_t ut_addr = reinterpret_cast<uint64_t>(p.unit_table + 2 * static_cast<int64_t>(b));
-    asm volatile("" : "+v"(ut_addr));           // a vector address: the load stays a vector load
-    typedef __attribute__((address_space(1))) const int32_t global_i32_t;
-    const global_i32_t* ut_ptr = reinterpret_cast<const global_i32_t*>(ut_addr);
-    int ux = ut_ptr[0], uy = ut_ptr[1];
-    const int per = p.splits / p.batch;
-    const int2 guess = make_int2(b * per, per);
-    r = merge16_partial<kUnits, kShared>(p, b, h, cb, guess, g, G);
-    // the guess's result and the entry are both in hand here (the compiler
-    // would otherwise compute on the table's range alone, after its load)
-    asm volatile("" : "+v"(r.m), "+v"(r.tot), "+v"(ux), "+v"(uy));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(r.acc[i]));
-    const int2 ut = make_int2(__builtin_amdgcn_readfirstlane(ux), __builtin_amdgcn_readfirstlane(uy));
-    if (ut.x != guess.x || ut.y != guess.y) r = merge16_partial<kUnits, kShared>(p, b, h, cb, ut, g, G);
+    // The sequence's units come from the unit table by a scalar load; the
+    // lse, scale and split-output loads then share one round trip.  (Loading
+    // the uniform map's range while the table is on its way gained nothing
+    // on equal lengths and, being wasted on ragged ones, doubled the
+    // traffic there.)
+    typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+    const const_i32_t* e = (const const_i32_t*)(p.unit_table + 2 * static_cast<int64_t>(b));
+    r = merge16_partial<kUnits, kShared>(p, b, h, cb, make_int2(e[0], e[1]), g, G);
   } else {
     r = merge16_partial<kUnits, kShared>(p, b, h, cb, make_int2(0, p.splits), g, G);
   }
