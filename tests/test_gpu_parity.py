@@ -571,20 +571,24 @@ def _balanced_lens(kind):
     raise ValueError(kind)
 
 
+@pytest.mark.parametrize("cfg_name", ["ragged_tp2", "kimi_k2_32k"])
 @pytest.mark.parametrize("kind", ["c5_mix", "min_max", "more_than_cus"])
-def test_balanced_units_table_and_parity(kind):
-    """The automatic plan of the 128-head d_s = 256 kernel: its unit table
-    against the brute-force unit map, and every sequence against the oracle."""
+def test_balanced_units_table_and_parity(kind, cfg_name):
+    """The automatic plan of the 128-head d_s = 256 and 64-head d_s = 128
+    kernels (one head group per workgroup, so about one unit per CU): the
+    unit table against the brute-force unit map, and every sequence against
+    the oracle."""
     lens = _balanced_lens(kind)
-    case = make_case(CONFIGS["ragged_tp2"], batch=len(lens), ctx=lens, seed=77)
-    print(f"balanced units: {kind}, batch {len(lens)}, max len {max(lens)}", flush=True)
+    case = make_case(CONFIGS[cfg_name], batch=len(lens), ctx=lens, seed=77)
+    tp = case.cfg.tp
+    print(f"balanced units: {cfg_name} {kind}, batch {len(lens)}, max len {max(lens)}", flush=True)
     o, l, table = balanced_shard_decode(case, g=1)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     _, want = unit_map_reference(case.seq_lens, cus, 1024, int(case.seq_lens.max()))
     assert np.array_equal(table.astype(np.int64), want)
     worst = 0.0
     for b in range(case.cfg.batch):
-        _, parts = oracle_step(case, b, 2, hadamard=True)
+        _, parts = oracle_step(case, b, tp, hadamard=True)
         err = rel_err(o[b].astype(np.float64), parts[1][0])
         worst = max(worst, err)
         assert err <= TOL_BF16, (b, int(case.seq_lens[b]))
@@ -592,14 +596,17 @@ def test_balanced_units_table_and_parity(kind):
     print(f"  worst max|err|/max|ref| {worst:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("cfg_name", ["dsv3_4k", "kimi_k2_32k"])
 @pytest.mark.parametrize("lens", [[1, 2, 63, 64], [65, 127, 128, 129], [4096, 1, 1000, 3]])
-def test_decode_bf16_edge_lengths(lens):
-    cases = [make_case(CONFIGS["dsv3_4k"], batch=1, ctx=L, seed=41 + i)
+def test_decode_bf16_edge_lengths(lens, cfg_name):
+    """Lengths at and around the 64-token tile, one sequence per call (a
+    single unit), on the 128-head and the 64-head kernels."""
+    cases = [make_case(CONFIGS[cfg_name], batch=1, ctx=L, seed=41 + i)
              for i, L in enumerate(lens)]
     for c in cases:
         gc = GpuCase(c)
         combined, _, _ = run_step(gc, hadamard=True)
-        ref, _ = oracle_step(c, 0, 2, hadamard=True)
+        ref, _ = oracle_step(c, 0, c.cfg.tp, hadamard=True)
         assert rel_err(host_f64(combined)[0], ref) <= TOL_BF16, int(c.seq_lens[0])
 
 
