@@ -35,8 +35,8 @@
 //                 P^T from ptile[i % 2]), V^T fragments of tile i+1 from
 //                 K buffer (i+1) % NB, then wait for tile i+2
 // so every copy has NB - 1 steps to land and NB - 2 tiles are in flight
-// while one is read.  128 heads over 256 columns: 40 KiB tiles, NB = 3;
-// 64 heads over 128 columns: 24 KiB tiles, NB = 5.
+// while one is read (NB = 3 for both shapes: 40 KiB tiles for 128 heads
+// over 256 columns, 24 KiB tiles for 64 heads over 128 columns).
 //
 // * Tile rows in LDS: 16-byte chunk c of row r sits at (c & ~7) |
 //   ((c & 7) ^ swz(r)), which keeps the score A-fragment reads (16 rows, one
@@ -179,7 +179,7 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   constexpr int NPF = NS * 4;               // P^T fragments per tile: (head tile, 16 tokens)
   constexpr int HF = NPF / 2;               // ... of tokens 0..31 (the rest: 32..63)
   static_assert((NS == 4 || NS == 2) && NV == 4, "two or four score waves, four value waves");
-  static_assert(NB == 3 || NB == 5, "K buffers");
+  static_assert(NB >= 2 && NB <= 6, "K buffers");
   static_assert(SLOTS % (4 * 64) == 0, "tile must split evenly over the copying waves");
   static_assert(CPR % 8 == 0 && DS % 64 == 0 && DR % 16 == 0, "shape");
   static_assert(MPW == 1 || MPW == 2, "value waves own one or two latent tiles");
@@ -703,23 +703,29 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
   }
 }
 
-// Tuning of the launches below (kept as named constants so the choice is
-// visible in one place).
-constexpr int kRolesKPre = 4, kRolesPPre = 3, kRolesPrioS = 1, kRolesPrioV = 0;
-constexpr int kRolesPro = 2;
+// Launch of HG heads per workgroup with a d_s-wide latent slice, NB K
+// buffers and the tuning T (LDS read distances of the K and P^T fragments,
+// wave priorities of the two roles, tiles copied before the first barrier).
+template <int KPRE, int PPRE, int PRIO_S, int PRIO_V, int PRO>
+struct Tuning {};
 
-// HG heads per workgroup with a d_s-wide latent slice and NB K buffers: 128
-// heads over 256 columns (40 KiB tiles, three buffers) or 64 heads over 128
-// columns (24 KiB tiles, five buffers, four tiles in flight).
-template <int HG, int DS, int NB>
-hipError_t launch_roles_t(const DecodeParams& p, hipStream_t s) {
+template <int HG, int DS, int NB, int KPRE, int PPRE, int PRIO_S, int PRIO_V, int PRO>
+hipError_t launch_roles_t(const DecodeParams& p, hipStream_t s, Tuning<KPRE, PPRE, PRIO_S, PRIO_V, PRO>) {
   const int n_units = p.max_units * (p.heads / HG);
   const int per_xcd = (n_units + 7) / 8;
-  hipLaunchKernelGGL((decode_roles_kernel<HG, DS, 64, NB, kRolesKPre, kRolesPPre, kRolesPrioS, kRolesPrioV,
-                                         kRolesPro>),
+  hipLaunchKernelGGL((decode_roles_kernel<HG, DS, 64, NB, KPRE, PPRE, PRIO_S, PRIO_V, PRO>),
                      dim3(8 * per_xcd), dim3((HG / 32 + 4) * 64), 0, s, p, n_units, per_xcd);
   return hipGetLastError();
 }
+
+// 128 heads over 256 columns: 40 KiB tiles, three buffers.  Score waves at
+// wave priority 1 (A/B on the DeepSeek-V3 shard).
+using kTune128 = Tuning<4, 3, 1, 0, 2>;
+// 64 heads over 128 columns: 24 KiB tiles, three buffers (A/B on the
+// Kimi-K2 shard: two, three, four and five buffers 55.2, 46.6, 47.6 and
+// 48.5 us per call: more tiles in flight stream slower).
+using kTune64 = Tuning<4, 3, 1, 0, 2>;
+constexpr int kNB64 = 3;
 
 }  // namespace
 
@@ -740,8 +746,8 @@ hipError_t launch_decode_roles(const DecodeParams& p, hipStream_t s) {
   if (p.chunk > kMaxTiles * kTile || p.chunk % kTile != 0 || p.max_units < 1 ||
       (p.unit_target == 0 && p.chunk < kTile) || p.unit_table == nullptr)
     return hipErrorInvalidValue;
-  if (p.d_s == 256) return launch_roles_t<128, 256, 3>(p, s);
-  return launch_roles_t<64, 128, 5>(p, s);
+  if (p.d_s == 256) return launch_roles_t<128, 256, 3>(p, s, kTune128{});
+  return launch_roles_t<64, 128, kNB64>(p, s, kTune64{});
 }
 
 }  // namespace tpla
