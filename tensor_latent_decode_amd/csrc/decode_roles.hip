@@ -162,7 +162,7 @@ struct CopyJob {
   uint32_t lds;
 };
 
-template <int HG, int DS, int DR, int NB, int KPRE, int PPRE, int PRIO_S, int PRIO_V, int kPro>
+template <int HG, int DS, int DR, int NB, int KPRE, int PPRE, int PRIO_S, int PRIO_V, int kPro, bool kLate>
 __global__ __attribute__((amdgpu_flat_work_group_size((HG / 32 + 4) * 64, (HG / 32 + 4) * 64),
                           amdgpu_waves_per_eu(2, 2)))
 void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
@@ -579,7 +579,7 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
         if (kCopy) {
 #pragma unroll
           for (int ci = 0; ci < IPT; ++ci)
-            if ((ci * NPF) / IPT == f) copy_chunk(cj, src_off, lq, ci);
+            if ((kLate ? NPF / 2 + (ci * (NPF / 2)) / IPT : (ci * NPF) / IPT) == f) copy_chunk(cj, src_off, lq, ci);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -705,26 +705,30 @@ void decode_roles_kernel(DecodeParams p, int n_units, int units_per_xcd) {
 
 // Launch of HG heads per workgroup with a d_s-wide latent slice, NB K
 // buffers and the tuning T (LDS read distances of the K and P^T fragments,
-// wave priorities of the two roles, tiles copied before the first barrier).
-template <int KPRE, int PPRE, int PRIO_S, int PRIO_V, int PRO>
+// wave priorities of the two roles, tiles copied before the first barrier,
+// and whether a step's tile copies ride on the second half of its value
+// fragments instead of all of them).
+template <int KPRE, int PPRE, int PRIO_S, int PRIO_V, int PRO, bool LATE>
 struct Tuning {};
 
-template <int HG, int DS, int NB, int KPRE, int PPRE, int PRIO_S, int PRIO_V, int PRO>
-hipError_t launch_roles_t(const DecodeParams& p, hipStream_t s, Tuning<KPRE, PPRE, PRIO_S, PRIO_V, PRO>) {
+template <int HG, int DS, int NB, int KPRE, int PPRE, int PRIO_S, int PRIO_V, int PRO, bool LATE>
+hipError_t launch_roles_t(const DecodeParams& p, hipStream_t s, Tuning<KPRE, PPRE, PRIO_S, PRIO_V, PRO, LATE>) {
   const int n_units = p.max_units * (p.heads / HG);
   const int per_xcd = (n_units + 7) / 8;
-  hipLaunchKernelGGL((decode_roles_kernel<HG, DS, 64, NB, KPRE, PPRE, PRIO_S, PRIO_V, PRO>),
+  hipLaunchKernelGGL((decode_roles_kernel<HG, DS, 64, NB, KPRE, PPRE, PRIO_S, PRIO_V, PRO, LATE>),
                      dim3(8 * per_xcd), dim3((HG / 32 + 4) * 64), 0, s, p, n_units, per_xcd);
   return hipGetLastError();
 }
 
 // 128 heads over 256 columns: 40 KiB tiles, three buffers.  Score waves at
 // wave priority 1 (A/B on the DeepSeek-V3 shard).
-using kTune128 = Tuning<4, 3, 1, 0, 2>;
+using kTune128 = Tuning<4, 3, 1, 0, 2, false>;
 // 64 heads over 128 columns: 24 KiB tiles, three buffers (A/B on the
 // Kimi-K2 shard: two, three, four and five buffers 55.2, 46.6, 47.6 and
-// 48.5 us per call: more tiles in flight stream slower).
-using kTune64 = Tuning<4, 3, 1, 0, 2>;
+// 48.5 us per call: more tiles in flight stream slower), a step's copies
+// on the second half of its value fragments (-0.5 us there; no gain on the
+// 128-head shard, +0.8 us on the ragged one).
+using kTune64 = Tuning<4, 3, 1, 0, 2, true>;
 constexpr int kNB64 = 3;
 
 }  // namespace
