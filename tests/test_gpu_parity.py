@@ -402,6 +402,8 @@ SHAPES = [  # (heads, d_c, tp, d_r)
     (128, 512, 1, 64),      # plain MLA, one device
     (48, 512, 1, 64),       # plain MLA in 16-head groups (Kimi-K2 under TP=4 has 16)
     (96, 512, 1, 64),       # plain MLA in 32-head groups
+    (128, 512, 4, 64),      # two 64-head groups per unit (d_s = 128)
+    (256, 512, 2, 64),      # two 128-head groups per unit (d_s = 256)
 ]
 
 
